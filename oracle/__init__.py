@@ -1,0 +1,16 @@
+"""fp64 CPU oracle of the Whisper audio-encoder forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it.  The product path (the HIP
+library and its binding) never calls it and shares no code with it.
+"""
+from .encoder import (  # noqa: F401
+    attention,
+    conv1d,
+    encode,
+    encoder_block,
+    gelu,
+    layer_norm,
+    mha,
+    softmax_rows,
+)

@@ -1,0 +1,185 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the
+independent torch-layer statement of the encoder notices each one.
+
+This measures the strength of the end-to-end pin: a dropped term, a wrong
+sign or index, or a transposed operand anywhere in the composition must move
+the output beyond the fp64 agreement the unmutated oracle reaches.
+"""
+import numpy as np
+import pytest
+from scipy.special import erf
+
+import oracle
+import oracle.encoder as enc
+from tests.test_oracle_pins import _small_cfg, _small_inputs
+from tests.torch_reference import torch_encode
+
+_orig = {n: getattr(enc, n) for n in ("conv1d", "gelu", "layer_norm", "softmax_rows", "attention", "mha",
+                                        "encoder_block")}
+
+
+def _conv_flipped(x, w, b, stride, pad=1):
+    return _orig["conv1d"](x, np.asarray(w)[:, :, ::-1], b, stride, pad)
+
+
+def _conv_shifted(x, w, b, stride, pad=1):
+    # reads frame stride*t + j instead of stride*t + j - 1
+    y = _orig["conv1d"](np.vstack([np.asarray(x, dtype=np.float64)[1:], np.zeros((1, np.shape(x)[1]))]),
+                        w, b, stride, pad)
+    return y
+
+
+def _gelu_tanh(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * z * (1 + np.tanh(np.sqrt(2 / np.pi) * (z + 0.044715 * z ** 3)))
+
+
+def _ln_unbiased(x, g, b, eps):
+    x = np.asarray(x, dtype=np.float64)
+    mu = x.mean(-1, keepdims=True)
+    var = x.var(-1, ddof=1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * g + b
+
+
+def _ln_eps_outside(x, g, b, eps):
+    x = np.asarray(x, dtype=np.float64)
+    mu = x.mean(-1, keepdims=True)
+    return (x - mu) / (np.sqrt(((x - mu) ** 2).mean(-1, keepdims=True)) + eps) * g + b
+
+
+def _ln_no_bias(x, g, b, eps):
+    return _orig["layer_norm"](x, g, np.zeros_like(np.asarray(b, dtype=np.float64)), eps)
+
+
+def _attn_unscaled(q, k, v):
+    return _orig["softmax_rows"](np.asarray(q) @ np.asarray(k).T) @ np.asarray(v)
+
+
+def _attn_wrong_axis(q, k, v):
+    s = np.asarray(q) @ np.asarray(k).T / 8.0
+    e = np.exp(s - s.max(axis=0, keepdims=True))
+    return (e / e.sum(axis=0, keepdims=True)) @ np.asarray(v)
+
+
+def _attn_causal(q, k, v):
+    s = np.asarray(q) @ np.asarray(k).T / 8.0
+    s = s + np.triu(np.full(s.shape, -np.inf), 1)
+    return _orig["softmax_rows"](s) @ np.asarray(v)
+
+
+def _mha_drop(field):
+    def f(xn, p, n_head):
+        p = dict(p)
+        p[field] = np.zeros_like(np.asarray(p[field], dtype=np.float64))
+        return _orig["mha"](xn, p, n_head)
+    return f
+
+
+def _mha_k_bias(xn, p, n_head):
+    # A bias on k adds q.c to every score of a query's row, which the softmax
+    # cancels: the output must NOT move (why a zero k bias is a safe reading).
+    xn = np.asarray(xn, dtype=np.float64)
+    d = xn.shape[1]
+    hd = d // n_head
+    q = xn @ p["wq"].T + p["bq"]
+    k = xn @ p["wk"].T + np.asarray(p["bq"], dtype=np.float64)
+    v = xn @ p["wv"].T + p["bv"]
+    ao = np.empty_like(q)
+    for h in range(n_head):
+        c = slice(h * hd, (h + 1) * hd)
+        ao[:, c] = enc.attention(q[:, c], k[:, c], v[:, c])
+    return ao @ p["wo"].T + p["bo"]
+
+
+def _mha_wo_transposed(xn, p, n_head):
+    p = dict(p)
+    p["wo"] = np.asarray(p["wo"]).T
+    return _orig["mha"](xn, p, n_head)
+
+
+def _mha_heads_interleaved(xn, p, n_head):
+    xn = np.asarray(xn, dtype=np.float64)
+    q = xn @ p["wq"].T + p["bq"]
+    k = xn @ p["wk"].T
+    v = xn @ p["wv"].T + p["bv"]
+    ao = np.empty_like(q)
+    for h in range(n_head):
+        c = slice(h, None, n_head)
+        ao[:, c] = enc.attention(q[:, c], k[:, c], v[:, c])
+    return ao @ p["wo"].T + p["bo"]
+
+
+def _block_no_mlp_residual(x, p, n_head, eps):
+    x = np.asarray(x, dtype=np.float64)
+    x = x + enc.mha(enc.layer_norm(x, p["ln1_g"], p["ln1_b"], eps), p, n_head)
+    xn = enc.layer_norm(x, p["ln2_g"], p["ln2_b"], eps)
+    return enc.gelu(xn @ p["fc1_w"].T + p["fc1_b"]) @ p["fc2_w"].T + p["fc2_b"]
+
+
+def _block_post_ln(x, p, n_head, eps):
+    x = np.asarray(x, dtype=np.float64)
+    x = enc.layer_norm(x + enc.mha(x, p, n_head), p["ln1_g"], p["ln1_b"], eps)
+    return enc.layer_norm(x + enc.gelu(x @ p["fc1_w"].T + p["fc1_b"]) @ p["fc2_w"].T + p["fc2_b"],
+                          p["ln2_g"], p["ln2_b"], eps)
+
+
+def _gelu_erf_no_sqrt2(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * z * (1 + erf(z))
+
+
+MUTATIONS = {
+    "conv taps flipped": ("conv1d", _conv_flipped),
+    "conv frame offset": ("conv1d", _conv_shifted),
+    "tanh GELU": ("gelu", _gelu_tanh),
+    "GELU missing sqrt2": ("gelu", _gelu_erf_no_sqrt2),
+    "LN unbiased variance": ("layer_norm", _ln_unbiased),
+    "LN eps outside sqrt": ("layer_norm", _ln_eps_outside),
+    "LN bias dropped": ("layer_norm", _ln_no_bias),
+    "attention unscaled": ("attention", _attn_unscaled),
+    "softmax over queries": ("attention", _attn_wrong_axis),
+    "causal mask": ("attention", _attn_causal),
+    "q bias dropped": ("mha", _mha_drop("bq")),
+    "v bias dropped": ("mha", _mha_drop("bv")),
+    "out_proj transposed": ("mha", _mha_wo_transposed),
+    "heads interleaved": ("mha", _mha_heads_interleaved),
+    "MLP residual dropped": ("encoder_block", _block_no_mlp_residual),
+    "post-LN block": ("encoder_block", _block_post_ln),
+}
+
+
+@pytest.fixture(scope="module")
+def case():
+    cfg = _small_cfg()
+    mel, params = _small_inputs(cfg, scale_attn=6.0)
+    ref = torch_encode(mel, params, cfg.n_layer, cfg.n_head, cfg.ln_eps)
+    return cfg, mel, params, ref
+
+
+def test_unmutated_agrees(case):
+    cfg, mel, params, ref = case
+    assert np.abs(oracle.encode(mel, params, cfg.n_layer, cfg.n_head) - ref).max() < 1e-10
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(case, name, monkeypatch):
+    cfg, mel, params, ref = case
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(enc, attr, fn)
+    got = enc.encode(mel, params, cfg.n_layer, cfg.n_head)
+    assert np.abs(got - ref).max() > 1e-6, name
+
+
+def test_missing_pieces_caught(case, monkeypatch):
+    """Dropping positions or the final LN also breaks agreement."""
+    cfg, mel, params, ref = case
+    p2 = dict(params)
+    p2["pos"] = np.zeros_like(params["pos"])
+    assert np.abs(enc.encode(mel, p2, cfg.n_layer, cfg.n_head) - ref).max() > 1e-6
+    assert np.abs(enc.encode(mel, params, cfg.n_layer, cfg.n_head, final_ln=False) - ref).max() > 1e-6
+
+
+def test_k_bias_is_unobservable(case, monkeypatch):
+    cfg, mel, params, ref = case
+    monkeypatch.setattr(enc, "mha", _mha_k_bias)
+    assert np.abs(enc.encode(mel, params, cfg.n_layer, cfg.n_head) - ref).max() < 1e-9

@@ -1,0 +1,278 @@
+"""Pins of the fp64 oracle against facts fixed outside it.
+
+Each test checks the oracle against the pages' shape facts (golden fixtures),
+closed forms, invariants, brute-force sums on tiny inputs, or an independent
+library implementation (torch float64 layers).  None retypes the oracle's
+own formula as its expectation.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from tests.conftest import read_golden
+from tests.torch_reference import torch_encode
+from whisper_audio_encoder_amd import synth
+from whisper_audio_encoder_amd.configs import CONFIGS, EncoderConfig
+
+
+# ----------------------------------------------------------------- conv (P-a)
+def _brute_conv(x, w, b, stride, pad=1):
+    """Pure-Python direct sum over taps and input channels."""
+    T_in, C_in = len(x), len(x[0])
+    C_out, _, K = w.shape
+    T_out = (T_in + 2 * pad - K) // stride + 1
+    y = [[0.0] * C_out for _ in range(T_out)]
+    for t in range(T_out):
+        for o in range(C_out):
+            acc = float(b[o])
+            for j in range(K):
+                src = stride * t + j - pad
+                if 0 <= src < T_in:
+                    for c in range(C_in):
+                        acc += float(w[o, c, j]) * float(x[src][c])
+            y[t][o] = acc
+    return np.array(y)
+
+
+@pytest.mark.parametrize("T_in,stride", [(8, 1), (9, 1), (8, 2), (17, 2), (16, 2)])
+def test_conv_brute_force(T_in, stride):
+    rng = np.random.default_rng(T_in * 10 + stride)
+    x = rng.standard_normal((T_in, 3))
+    w = rng.standard_normal((4, 3, 3))
+    b = rng.standard_normal(4)
+    got = oracle.conv1d(x, w, b, stride)
+    np.testing.assert_allclose(got, _brute_conv(x, w, b, stride), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("stride", [1, 2])
+def test_conv_matches_torch(stride):
+    rng = np.random.default_rng(7 + stride)
+    x = rng.standard_normal((31, 5))
+    w = rng.standard_normal((6, 5, 3))
+    b = rng.standard_normal(6)
+    ref = F.conv1d(torch.from_numpy(x.T[None].copy()), torch.from_numpy(w), torch.from_numpy(b),
+                   stride=stride, padding=1)[0].T.numpy()
+    np.testing.assert_allclose(oracle.conv1d(x, w, b, stride), ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("stride", [1, 2])
+def test_conv_delta_input(stride):
+    """A unit impulse at (t0, c) reproduces the taps W[:, c, j] at the outputs
+    whose window covers t0, and the bias elsewhere (no kernel flip)."""
+    T_in, C_in, C_out = 12, 3, 4
+    rng = np.random.default_rng(3)
+    w = rng.standard_normal((C_out, C_in, 3))
+    b = rng.standard_normal(C_out)
+    t0, c = 5, 1
+    x = np.zeros((T_in, C_in))
+    x[t0, c] = 1.0
+    y = oracle.conv1d(x, w, b, stride)
+    for t in range(y.shape[0]):
+        expect = b.copy()
+        for j in range(3):
+            if stride * t + j - 1 == t0:
+                expect = expect + w[:, c, j]
+        np.testing.assert_array_equal(y[t], expect)
+
+
+def test_stem_lengths_golden():
+    rows = read_golden("stem_shapes.txt")
+    for name, k, s, p, t_in, t_out in rows:
+        k, s, p, t_in, t_out = map(int, (k, s, p, t_in, t_out))
+        x = np.zeros((t_in, 2))
+        w = np.zeros((1, 2, k))
+        assert oracle.conv1d(x, w, np.zeros(1), s, pad=p).shape == (t_out, 1), name
+    # the general even-length rule of the stride-2 layer
+    for t_in in (2, 10, 100, 3000):
+        assert oracle.conv1d(np.zeros((t_in, 1)), np.zeros((1, 1, 3)), np.zeros(1), 2).shape[0] == t_in // 2
+
+
+# ----------------------------------------------------------------- GELU (P-b)
+def test_gelu_normal_cdf_golden():
+    for xs, phis in read_golden("normal_cdf.txt"):
+        x, phi = float(xs), float(phis)
+        assert abs(oracle.gelu(x) - x * phi) < 1e-15
+        assert abs(oracle.gelu(-x) - (-x) * (1.0 - phi)) < 1e-15
+
+
+def test_gelu_identities_and_libm():
+    x = np.linspace(-9, 9, 2001)
+    g = oracle.gelu(x)
+    # erf is odd, so gelu(x) - gelu(-x) = x
+    np.testing.assert_allclose(g - oracle.gelu(-x), x, rtol=0, atol=1e-14)
+    assert oracle.gelu(0.0) == 0.0
+    ref = np.array([0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0))) for v in x])
+    np.testing.assert_allclose(g, ref, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(g, F.gelu(torch.from_numpy(x), approximate="none").numpy(), rtol=0, atol=1e-15)
+
+
+def test_gelu_is_not_tanh_form():
+    x = np.linspace(-6, 6, 4001)
+    tanh_form = F.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    assert np.abs(oracle.gelu(x) - tanh_form).max() > 1e-4
+
+
+# ------------------------------------------------------------ LayerNorm (P-c)
+def test_layer_norm_invariants():
+    rng = np.random.default_rng(11)
+    d, eps = 384, 1e-5
+    x = rng.standard_normal((50, d)) * rng.uniform(0.1, 3, (50, 1)) + rng.uniform(-2, 2, (50, 1))
+    y = oracle.layer_norm(x, np.ones(d), np.zeros(d), eps)
+    assert np.abs(y.mean(axis=1)).max() < 1e-12
+    # population variance of the output is sigma^2 / (sigma^2 + eps)
+    s2 = x.var(axis=1)
+    np.testing.assert_allclose(y.var(axis=1), s2 / (s2 + eps), rtol=1e-12)
+    # a constant row normalises to zero, leaving the bias
+    beta = rng.standard_normal(d)
+    const = oracle.layer_norm(np.full((1, d), 3.25), rng.standard_normal(d), beta, eps)
+    np.testing.assert_allclose(const[0], beta, rtol=0, atol=1e-15)
+
+
+def test_layer_norm_matches_torch():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((33, 96))
+    g, b = rng.standard_normal(96), rng.standard_normal(96)
+    ref = F.layer_norm(torch.from_numpy(x), (96,), torch.from_numpy(g), torch.from_numpy(b), 1e-5).numpy()
+    np.testing.assert_allclose(oracle.layer_norm(x, g, b, 1e-5), ref, rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------ attention (P-d)
+def _brute_attention(q, k, v):
+    T, hd = q.shape
+    out = np.zeros((T, v.shape[1]))
+    for t in range(T):
+        s = [sum(q[t, e] * k[u, e] for e in range(hd)) / math.sqrt(hd) for u in range(len(k))]
+        m = max(s)
+        p = [math.exp(x - m) for x in s]
+        z = sum(p)
+        for u in range(len(k)):
+            out[t] += (p[u] / z) * v[u]
+    return out
+
+
+@pytest.mark.parametrize("T", [7, 33])
+def test_attention_brute_force(T):
+    rng = np.random.default_rng(T)
+    q, k, v = (rng.standard_normal((T, 64)) for _ in range(3))
+    np.testing.assert_allclose(oracle.attention(q, k, v), _brute_attention(q, k, v), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("T", [7, 33, 130])
+def test_attention_matches_torch_sdpa(T):
+    rng = np.random.default_rng(100 + T)
+    q, k, v = (rng.standard_normal((T, 64)) * 2 for _ in range(3))
+    ref = F.scaled_dot_product_attention(*(torch.from_numpy(a)[None] for a in (q, k, v)))[0].numpy()
+    np.testing.assert_allclose(oracle.attention(q, k, v), ref, rtol=0, atol=1e-12)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(5)
+    T = 130
+    v = rng.standard_normal((T, 64))
+    q = rng.standard_normal((T, 64))
+    # identical keys, or a zero query: every weight is 1/T
+    k_same = np.tile(rng.standard_normal(64), (T, 1))
+    np.testing.assert_allclose(oracle.attention(q, k_same, v), np.tile(v.mean(0), (T, 1)), atol=1e-13)
+    np.testing.assert_allclose(oracle.attention(np.zeros((T, 64)), rng.standard_normal((T, 64)), v),
+                               np.tile(v.mean(0), (T, 1)), atol=1e-13)
+    # one key 40 score units above the rest selects its value row
+    k = np.zeros((T, 64))
+    k[17] = 1.0
+    q1 = np.full((1, 64), 40.0 * 8.0 / 64.0)  # q.k / 8 = 40 for key 17, 0 elsewhere
+    np.testing.assert_allclose(oracle.attention(q1, k, v)[0], v[17], atol=1e-14)
+    # the score matrix rows are probability vectors
+    p = oracle.softmax_rows(rng.standard_normal((9, T)) * 10)
+    np.testing.assert_allclose(p.sum(1), 1.0, atol=1e-14)
+    assert (p >= 0).all()
+
+
+def test_attention_permutation_equivariant():
+    rng = np.random.default_rng(8)
+    T = 40
+    q, k, v = (rng.standard_normal((T, 64)) for _ in range(3))
+    perm = rng.permutation(T)
+    base = oracle.attention(q, k, v)
+    np.testing.assert_allclose(oracle.attention(q[perm], k[perm], v[perm]), base[perm], atol=1e-13)
+    # permuting keys and values together leaves the output unchanged (no mask, no positions)
+    np.testing.assert_allclose(oracle.attention(q, k[perm], v[perm]), base, atol=1e-13)
+
+
+# ------------------------------------------------------ block / encoder (P-e)
+def _small_cfg(**kw):
+    base = dict(name="pin", batch=1, n_mels=16, d_model=128, n_head=2, d_ff=512, n_layer=2,
+                seed=77, n_frames=40, n_ctx=20)
+    base.update(kw)
+    return EncoderConfig(**base)
+
+
+def _small_inputs(cfg, scale_attn=1.0):
+    mel, params = synth.make_inputs(cfg)
+    params = {k: v.astype(np.float64) for k, v in params.items()}
+    for li in range(cfg.n_layer):
+        # sharpen the attention so the test is sensitive to the score path
+        params[f"l{li}.wq"] *= scale_attn
+        params[f"l{li}.wk"] *= scale_attn
+    return mel[0].astype(np.float64), params
+
+
+def test_block_identity_when_outputs_zero():
+    cfg = _small_cfg(n_layer=1)
+    _, params = _small_inputs(cfg)
+    p = {k.split(".", 1)[1]: v for k, v in params.items() if k.startswith("l0.")}
+    for f in ("wo", "bo", "fc2_w", "fc2_b"):
+        p[f] = np.zeros_like(p[f])
+    x = np.random.default_rng(1).standard_normal((cfg.n_ctx, cfg.d_model))
+    np.testing.assert_array_equal(oracle.encoder_block(x, p, cfg.n_head, cfg.ln_eps), x)
+
+
+def test_zero_layers_is_ln_of_stem():
+    cfg = _small_cfg(n_layer=0)
+    mel, params = _small_inputs(cfg)
+    out = oracle.encode(mel, params, 0, cfg.n_head)
+    np.testing.assert_allclose(out, torch_encode(mel, params, 0, cfg.n_head), atol=1e-12)
+
+
+@pytest.mark.parametrize("final_ln", [True, False])
+def test_encoder_matches_torch_layers(final_ln):
+    cfg = _small_cfg()
+    mel, params = _small_inputs(cfg, scale_attn=6.0)
+    got = oracle.encode(mel, params, cfg.n_layer, cfg.n_head, cfg.ln_eps, final_ln=final_ln)
+    ref = torch_encode(mel, params, cfg.n_layer, cfg.n_head, cfg.ln_eps, final_ln=final_ln)
+    assert got.shape == (cfg.n_ctx, cfg.d_model)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-10)
+
+
+def test_encoder_taps_consistent():
+    cfg = _small_cfg()
+    mel, params = _small_inputs(cfg)
+    t = oracle.encode(mel, params, cfg.n_layer, cfg.n_head, taps=True)
+    assert t["c1"].shape == (cfg.n_frames, cfg.d_model)
+    assert t["x0"].shape == (cfg.n_ctx, cfg.d_model)
+    assert len(t["blocks"]) == cfg.n_layer
+    np.testing.assert_array_equal(t["out"], oracle.encode(mel, params, cfg.n_layer, cfg.n_head))
+
+
+# --------------------------------------------------------------- shapes (P-f)
+def test_family_golden_matches_configs():
+    fam = {r[0]: tuple(map(int, r[1:])) for r in read_golden("whisper_family.txt")}
+    pairs = {"c1": "tiny", "c2": "base", "c3": "small", "c4": "large-v3"}
+    for cname, fname in pairs.items():
+        c = CONFIGS[cname]
+        assert (c.n_layer, c.d_model, c.n_head, c.n_mels) == fam[fname], cname
+        assert c.d_model // c.n_head == 64 and c.d_ff == 4 * c.d_model
+    c0 = CONFIGS["c0"]
+    assert (c0.d_model, c0.n_head, c0.n_mels, c0.n_layer) == (384, 6, 80, 1)
+
+
+def test_full_window_shape():
+    """3000 x n_mels in, 1500 x d out, for a full-length window (one block)."""
+    cfg = CONFIGS["c0"]
+    mel, params = synth.make_inputs(cfg)
+    out = oracle.encode(mel[0], params, cfg.n_layer, cfg.n_head, cfg.ln_eps)
+    assert mel.shape == (1, 3000, 80) and out.shape == (1500, 384)
+    assert np.isfinite(out).all()

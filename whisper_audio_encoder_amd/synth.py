@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs shared by the oracle-side tests and the GPU path.
+
+This module draws random numbers and lays bytes out; it holds none of the
+encoder's arithmetic.  Both the fp64 oracle and the HIP library consume what it
+produces, so it is the only code the two sides have in common.
+
+Recipe (one generator per workload, numpy PCG64 seeded with the config seed):
+
+* mel: one ``[batch, n_frames, n_mels]`` draw of i.i.d. N(mean=-0.2, std=0.4),
+  clamped to [-1.5, 1.5], kept fp32.  Whisper's log-mel ends with an (x+4)/4
+  rescale into roughly [-1, 1] (CKE page, "The Frontend: Sound Becomes A
+  Tensor"), which this range imitates.
+* parameters, drawn after the mel in canonical blob order: matrices, conv
+  taps and biases N(0, 0.02); LayerNorm gains 1 + N(0, 0.02), LayerNorm
+  biases N(0, 0.02).  Everything is rounded to IEEE binary16.
+* positions: a stored table (whisper 0.9.0 API page, model.nu: the position
+  embedding is a stored tensor).  Its synthetic values are the sine/cosine
+  table whose frequency ladder omega_i = exp(-i * ln(10000) / (d/2 - 1)) is
+  the one the Whistle porting notes print for width 512 (section on the
+  decoder's memory positions): sines in the first d/2 columns, cosines in the
+  last d/2, computed in fp64 and rounded to fp16.
+
+Canonical blob (little-endian binary16, ``[out][in]`` row-major matrices,
+conv taps ``[out][in][k]``) in the field order of the ``Whisper`` struct on
+the whisper 0.9.0 API page (model.nu): conv1_w, conv1_b, conv2_w, conv2_b,
+pos, then per layer ln1_g, ln1_b, wq, bq, wk (no bias entry), wv, bv, wo, bo,
+ln2_g, ln2_b, fc1_w, fc1_b, fc2_w, fc2_b, and finally lnf_g, lnf_b.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .configs import EncoderConfig
+
+LAYER_FIELDS = ("ln1_g", "ln1_b", "wq", "bq", "wk", "wv", "bv", "wo", "bo",
+                "ln2_g", "ln2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")
+
+
+def param_shapes(cfg: EncoderConfig):
+    """Ordered (name, shape) list of the canonical blob."""
+    d, F, nm = cfg.d_model, cfg.d_ff, cfg.n_mels
+    out = [("conv1_w", (d, nm, 3)), ("conv1_b", (d,)),
+           ("conv2_w", (d, d, 3)), ("conv2_b", (d,)),
+           ("pos", (cfg.n_ctx, d))]
+    layer = {"ln1_g": (d,), "ln1_b": (d,), "wq": (d, d), "bq": (d,), "wk": (d, d),
+             "wv": (d, d), "bv": (d,), "wo": (d, d), "bo": (d,),
+             "ln2_g": (d,), "ln2_b": (d,), "fc1_w": (F, d), "fc1_b": (F,),
+             "fc2_w": (d, F), "fc2_b": (d,)}
+    for li in range(cfg.n_layer):
+        for f in LAYER_FIELDS:
+            out.append((f"l{li}.{f}", layer[f]))
+    out += [("lnf_g", (d,)), ("lnf_b", (d,))]
+    return out
+
+
+def weights_nbytes(cfg: EncoderConfig) -> int:
+    return 2 * sum(int(np.prod(s)) for _, s in param_shapes(cfg))
+
+
+def sinusoid_table(n_ctx: int, d: int) -> np.ndarray:
+    """fp64 sine/cosine table [n_ctx, d] (frequency ladder described above)."""
+    half = d // 2
+    omega = np.exp(-np.arange(half, dtype=np.float64) * (np.log(10000.0) / (half - 1)))
+    ang = np.arange(n_ctx, dtype=np.float64)[:, None] * omega[None, :]
+    return np.concatenate([np.sin(ang), np.cos(ang)], axis=1)
+
+
+def make_mel(rng: np.random.Generator, batch: int, n_frames: int, n_mels: int) -> np.ndarray:
+    mel = rng.normal(-0.2, 0.4, size=(batch, n_frames, n_mels))
+    return np.clip(mel, -1.5, 1.5).astype(np.float32)
+
+
+def make_params(rng: np.random.Generator, cfg: EncoderConfig) -> dict:
+    """Parameters in canonical order, each an fp16 numpy array."""
+    params = {}
+    for name, shape in param_shapes(cfg):
+        base = name.split(".")[-1]
+        if base == "pos":
+            params[name] = sinusoid_table(cfg.n_ctx, cfg.d_model).astype(np.float16)
+            continue
+        x = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(0.02)
+        if base.endswith("_g"):
+            x = x + np.float32(1.0)
+        params[name] = x.astype(np.float16)
+    return params
+
+
+def make_inputs(cfg: EncoderConfig, batch: int | None = None, seed: int | None = None):
+    """(mel fp32 [B, n_frames, n_mels], params dict of fp16 arrays)."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    B = cfg.batch if batch is None else batch
+    mel = make_mel(rng, B, cfg.n_frames, cfg.n_mels)
+    params = make_params(rng, cfg)
+    return mel, params
+
+
+def pack_blob(cfg: EncoderConfig, params: dict) -> np.ndarray:
+    """Concatenate parameters in canonical order into one uint8 blob."""
+    parts = []
+    for name, shape in param_shapes(cfg):
+        a = np.asarray(params[name])
+        if a.shape != tuple(shape) or a.dtype != np.float16:
+            raise ValueError(f"{name}: expected fp16 {shape}, got {a.dtype} {a.shape}")
+        parts.append(np.ascontiguousarray(a).reshape(-1))
+    return np.concatenate(parts).view(np.uint8)
+
+
+def layer_params(params: dict, li: int) -> dict:
+    return {f: params[f"l{li}.{f}"] for f in LAYER_FIELDS}
