@@ -1,0 +1,172 @@
+"""Throughput of the Whisper audio-encoder forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
+
+A step is one wenc_forward over one batch of synthetic windows (conv stem,
+all blocks, final LN), with the mel input and the weights already resident
+in device memory.  Prints ONE JSON line.  Per-launch kernel times come from
+HIP events the library records on the same stream around each launch of the
+dominant kernel during the timed steps; the fp64 oracle is timed on the
+host on a bounded sample for the cpu_baseline field.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "encoder 30s-windows/sec and TFLOP/s (% of fp16 MFMA peak), 1 MI355X"
+PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def site_work(cfg, B):
+    """Algorithmic FLOPs (MFMA sites) or HBM bytes (memory-bound sites) of one launch."""
+    T, F, d, nm, H, Fd = cfg.n_ctx, cfg.n_frames, cfg.d_model, cfg.n_mels, cfg.n_head, cfg.d_ff
+    M = B * T
+    return {
+        "conv1": ("mfma", 2.0 * B * F * d * 3 * nm),
+        "conv2": ("mfma", 2.0 * M * d * 3 * d),
+        "qkv": ("mfma", 2.0 * M * 3 * d * d),
+        "attn": ("mfma", 4.0 * B * H * T * T * 64),
+        "oproj": ("mfma", 2.0 * M * d * d),
+        "fc1": ("mfma", 2.0 * M * Fd * d),
+        "fc2": ("mfma", 2.0 * M * d * Fd),
+        # LN: read fp32 x, write fp16 (final: fp32); gains and biases are negligible
+        "ln1": ("hbm", M * d * (4.0 + 2.0)),
+        "ln2": ("hbm", M * d * (4.0 + 2.0)),
+        "lnf": ("hbm", M * d * (4.0 + 4.0)),
+        "ingest": ("hbm", B * F * nm * 4.0 + B * (F + 2) * nm * 2.0),
+    }
+
+
+def cpu_baseline(cfg, mel, params, budget_s=30.0):
+    """Time the fp64 oracle on one window of the workload (all blocks)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    t0 = time.perf_counter()
+    oracle.encode(mel[0], params, cfg.n_layer, cfg.n_head, cfg.ln_eps, bool(cfg.final_ln))
+    dt = time.perf_counter() - t0
+    return {"value": 1.0 / dt, "unit": "windows/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full window (batch item 0) of the same workload, fp64 numpy/OpenBLAS, {dt:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4", choices=["c0", "c1", "c2", "c3", "c4"])
+    ap.add_argument("--batch", type=int, default=None, help="override the workload's batch")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args(argv)
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the encoder shards by window (pure data parallelism, no "
+              "collective), and this build runs and reports a single MI355X only", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from whisper_audio_encoder_amd import synth, wenc
+    from whisper_audio_encoder_amd.configs import CONFIGS, WORKLOAD_NAMES
+
+    cfg = CONFIGS[a.workload]
+    B = a.batch or cfg.batch
+    log(f"[bench] workload {a.workload}: {WORKLOAD_NAMES[a.workload]}, batch {B}")
+    mel, params = synth.make_inputs(cfg, batch=B)
+    blob = synth.pack_blob(cfg, params)
+    enc = wenc.Encoder(cfg, blob, max_batch=B)
+    mel_d = torch.from_numpy(mel).to("cuda:0")
+    out = torch.empty((B, cfg.n_ctx, cfg.d_model), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    # warm-up with events around every launch: finds the dominant kernel
+    wenc.wenc_profile(enc.h, (1 << wenc.N_SITES) - 1)
+    for _ in range(a.warmup):
+        enc.forward(mel_d, out)
+    torch.cuda.synchronize()
+    warm = wenc.wenc_profile_read(enc.h)
+    mfma_sites = [s for s in wenc.SITES if site_work(cfg, B)[s][0] == "mfma"]
+    dominant = max(wenc.SITES, key=lambda s: warm[s][0])
+    total_warm = sum(v[0] for v in warm.values()) or 1.0
+    log("[bench] per-site share of kernel time (warm-up): " +
+        ", ".join(f"{s} {100 * warm[s][0] / total_warm:.1f}%" for s in wenc.SITES if warm[s][1]))
+
+    # timed region: events only around the dominant kernel's launches
+    wenc.wenc_profile(enc.h, 1 << wenc.SITES.index(dominant))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(a.steps):
+        enc.forward(mel_d, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / a.steps
+    prof = wenc.wenc_profile_read(enc.h)
+    wenc.wenc_profile(enc.h, 0)
+    log(f"[bench] {a.steps} steps: {ms:.3f} ms/step (wall {1e3 * wall / a.steps:.3f} ms/step)")
+
+    flops = cfg.flops_per_window() * B
+    tflops = flops / (ms * 1e-3) / 1e12
+    kind, work = site_work(cfg, B)[dominant]
+    d_ms, d_n = prof[dominant]
+    avg_s = d_ms / max(d_n, 1) * 1e-3
+    if kind == "mfma":
+        roof = {"bound": "mfma", "achieved": work / avg_s / 1e12, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": work / avg_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dominant
+    roof["avg_launch_ms"] = avg_s * 1e3
+    roof["launches"] = d_n
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on one window ...")
+        cpu = cpu_baseline(cfg, mel, params)
+        log(f"[bench] oracle: {cpu['value']:.4f} windows/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": B / (ms * 1e-3),
+        "unit": "windows/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded mel N(-0.2,0.4) clamped, random-init fp16 weights)",
+        "config": {"workload": f"{WORKLOAD_NAMES[a.workload]} ({a.workload})", "batch": B,
+                   "n_frames": cfg.n_frames, "n_ctx": cfg.n_ctx, "d_model": cfg.d_model, "n_head": cfg.n_head,
+                   "d_ff": cfg.d_ff, "n_layer": cfg.n_layer, "n_mels": cfg.n_mels, "parallelism": "single GPU"},
+        "tflops": tflops,
+        "pct_fp16_peak": 100.0 * tflops / PEAK_F16_TFLOPS,
+        "site_ms_per_step": {s: warm[s][0] / max(a.warmup, 1) for s in wenc.SITES if warm[s][1]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "host": platform.node(),
+    }
+    enc.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

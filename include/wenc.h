@@ -1,0 +1,193 @@
+/*
+ * wenc — the Whisper audio-encoder forward pass on one AMD Instinct MI355X
+ * (gfx950), behind a plain C ABI.
+ *
+ * What is computed (whisper 0.9.0 API page, section model.nu; CKE page "How
+ * Audio Becomes Words", the stitched-circuit figure):
+ *
+ *   mel [n_frames x n_mels] --conv1 (k3 s1 p1) + GELU--> [n_frames x d]
+ *       --conv2 (k3 s2 p1) + GELU--> [n_ctx x d] --+ stored positions-->
+ *   n_layer x [ x += out_proj(attn(LN1 x));  x += fc2(GELU(fc1(LN2 x))) ]
+ *       --final LN--> out [n_ctx x d]
+ *
+ * attention is non-causal multi-head attention with scores q.k/sqrt(64)
+ * (kernels.nu); k_proj has no bias (model.nu); GELU is the erf form
+ * (kernels.nu); LayerNorm has a bias (kernels.nu).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named "device" are HIP device addresses owned by the caller
+ *     (typically torch tensors); the library never frees them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Compute entry points only enqueue work on it and return without a host
+ *     synchronisation.
+ *   - Every int-returning call returns WENC_OK or a negative WENC_E* code;
+ *     wenc_last_error() gives the message.  Argument errors are detected on
+ *     the host before anything is enqueued.
+ *   - A handle serves one stream at a time: two overlapping wenc_forward
+ *     calls on one handle race on its scratch (one transcription at a time
+ *     per device, as the whisper README's serving notes describe).
+ */
+#ifndef WENC_H
+#define WENC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct wenc wenc_t;
+
+/* Encoder shape.  Shapes are read from the checkpoint in the pages' design
+ * (whisper README: nothing hardcoded to a model size); here the caller states
+ * them.  Constraints checked by wenc_create:
+ *   head_dim == 64, d_model == n_head * 64, n_mels % 8 == 0, d_ff % 8 == 0,
+ *   n_frames even and == 2 * n_ctx, n_layer >= 0, 1 <= max_batch,
+ *   max_batch * n_frames < 2^24, ln_eps > 0. */
+typedef struct wenc_config {
+    int32_t n_mels;     /* mel bins per frame (80; 128 for large-v3)          */
+    int32_t d_model;    /* width                                               */
+    int32_t n_head;     /* attention heads                                     */
+    int32_t head_dim;   /* must be 64                                          */
+    int32_t d_ff;       /* fc1 width (4 * d_model in Whisper)                  */
+    int32_t n_layer;    /* encoder blocks                                      */
+    int32_t n_frames;   /* mel frames per window (3000 for 30 s)               */
+    int32_t n_ctx;      /* encoder positions = n_frames / 2 (1500)             */
+    float   ln_eps;     /* LayerNorm epsilon (1e-5)                            */
+    int32_t final_ln;   /* 1: apply the final LN (the encoder ends in one)     */
+    int32_t max_batch;  /* windows per internal chunk; scratch is sized for it */
+} wenc_config;
+
+enum {
+    WENC_OK = 0,
+    WENC_EINVAL = -1, /* bad argument: config, size, null pointer, batch < 0 */
+    WENC_ENOMEM = -2, /* device allocation failed; message has bytes asked and free */
+    WENC_ENODEV = -3, /* no HIP device, or the device is not gfx950            */
+    WENC_ESTATE = -4, /* forward before wenc_load                              */
+    WENC_EHIP = -5    /* HIP runtime or launch error; message has its string   */
+};
+
+/* Validate `cfg`, allocate the device weight arena and the activation
+ * scratch for cfg->max_batch windows on the current HIP device.  On success
+ * *out owns them; on failure *out is NULL and wenc_last_error(NULL) explains
+ * (the whisper README's implementation notes: a failed device allocation is
+ * reported with the device's memory, never run past). */
+int wenc_create(const wenc_config *cfg, wenc_t **out);
+
+/* Exact byte size of the canonical weight blob for `cfg`, 0 if invalid.
+ * Blob: IEEE binary16, little-endian, in the field order of the Whisper
+ * struct on the whisper 0.9.0 API page (model.nu):
+ *   conv1_w [d][n_mels][3], conv1_b [d], conv2_w [d][d][3], conv2_b [d],
+ *   pos [n_ctx][d],
+ *   per layer: ln1_g [d], ln1_b [d], wq [d][d], bq [d], wk [d][d] (no bias
+ *   entry: k_proj has none), wv [d][d], bv [d], wo [d][d], bo [d],
+ *   ln2_g [d], ln2_b [d], fc1_w [d_ff][d], fc1_b [d_ff], fc2_w [d][d_ff],
+ *   fc2_b [d],
+ *   lnf_g [d], lnf_b [d].
+ * Matrices are [out][in] row-major (kernels.nu, wk_matvec: W[rows][cols]). */
+size_t wenc_weights_nbytes(const wenc_config *cfg);
+
+/* Copy a HOST blob (layout above) into the device arena, repacking it once
+ * (conv taps to [out][k][in], q|k|v concatenated with a zero k bias, gains,
+ * biases and positions widened exactly to fp32) in one upload.  nbytes must
+ * equal wenc_weights_nbytes.  Synchronous; may be called again between
+ * forwards to replace the weights.  The blob is not retained. */
+int wenc_load(wenc_t *h, const void *blob, size_t nbytes);
+
+/* out[b] = encoder(mel[b]) for b < batch.
+ *   mel: device, fp32 [batch][n_frames][n_mels], a frame contiguous
+ *        (whisper 0.9.0 API page, wh_encode).
+ *   out: device, fp32 [batch][n_ctx][d_model] row-major (wh_enc_out).
+ * batch == 0 is a no-op; batch > max_batch runs in chunks of max_batch.
+ * Enqueued on `stream`; no host synchronisation. */
+int wenc_forward(wenc_t *h, const float *mel, int32_t batch, float *out, void *stream);
+
+/* Release the handle and its device memory.  NULL-safe.  Synchronises the
+ * device first so no enqueued work still uses the memory. */
+void wenc_destroy(wenc_t *h);
+
+/* Message for the last failure on `h` (or of wenc_create / handle-less calls
+ * in this thread when h is NULL).  Never NULL; "" when there is none. */
+const char *wenc_last_error(const wenc_t *h);
+
+/* ------------------------------------------------------------------------
+ * Stage taps and kernel entry points.  They expose each step of the path in
+ * isolation so that it can be compared with an independent implementation
+ * (the CKE page: every kernel has its own parity oracle).  All pointers are
+ * device pointers; fp16 buffers are IEEE binary16 bit patterns (uint16_t).
+ * ---------------------------------------------------------------------- */
+
+/* Stage taps of wenc_forward (batch <= max_batch):
+ *   WENC_TAP_C1:    dst fp16 [batch][n_frames][d]   conv1 + GELU
+ *   WENC_TAP_STEM:  dst fp32 [batch][n_ctx][d]      conv2 + GELU + positions
+ *   WENC_TAP_BLOCK + l: dst fp32 [batch][n_ctx][d]  residual after block l  */
+enum { WENC_TAP_C1 = 0, WENC_TAP_STEM = 1, WENC_TAP_BLOCK = 2 };
+int wenc_forward_tap(wenc_t *h, const float *mel, int32_t batch, int32_t tap, void *dst, void *stream);
+
+/* LayerNorm over rows of x (kernels.nu: mean-subtracting, with bias):
+ *   y[r][i] = (x[r][i] - mean_r) / sqrt(var_r + eps) * gamma[i] + beta[i],
+ * population variance.  x fp32 [rows][d]; gamma, beta fp32 [d];
+ * y fp32 (out_f32 = 1) or fp16 [rows][d].  d % 4 == 0, d <= 2048. */
+int wenc_k_layernorm(const float *x, const float *gamma, const float *beta, void *y,
+                     int32_t rows, int32_t d, float eps, int32_t out_f32, void *stream);
+
+/* Epilogues of the fp16 MFMA GEMM  acc[m][n] = sum_k A[m][k] * W[n][k]. */
+enum {
+    WENC_EPI_GELU_F16 = 0, /* C fp16 = gelu(acc + bias)                       (fc1, conv1) */
+    WENC_EPI_CONV2 = 1,    /* C fp32 = gelu(acc + bias) + pos[m % pos_rows]   (conv2)      */
+    WENC_EPI_RESID = 2,    /* C fp32 += acc + bias                            (out_proj, fc2) */
+    WENC_EPI_QKV = 3       /* q, k, v^T scatter, see wenc_gemm_args           (qkv)        */
+};
+
+/* GEMM arguments.  Row m of A starts at
+ *   A + (m / a_rows_per_batch) * a_batch_stride + (m % a_rows_per_batch) * lda
+ * (elements), which expresses both plain row-major A (a_rows_per_batch = M,
+ * lda = K) and the conv stem's overlapping frame windows over a zero-padded,
+ * frame-contiguous input (lda = stride * C_in, K = 3 * C_in).  W is
+ * [N][ldw] row-major fp16 (K contiguous).  Output row m of C starts at
+ *   C + (m / c_rows_per_batch) * c_batch_stride
+ *     + (m % c_rows_per_batch + c_row_offset) * ldc.
+ * QKV: N = 3 * n_head * 64; columns [0, d) go to q and [d, 2d) to k as
+ * [batch][n_head][T][64] fp16, columns [2d, 3d) to vt as
+ * [batch][n_head][64][ldvt] fp16 (keys contiguous), with m = b * T + t;
+ * the q slice is multiplied by q_scale after its bias.  Requires K % 8 == 0,
+ * lda % 8 == 0, ldw % 8 == 0, a_batch_stride % 8 == 0, M * ... < 2^24. */
+typedef struct wenc_gemm_args {
+    const uint16_t *A; int64_t a_batch_stride; int32_t a_rows_per_batch; int32_t lda;
+    const uint16_t *W; int32_t ldw;
+    const float *bias;           /* [N] fp32, never NULL                        */
+    void *C; int64_t c_batch_stride; int32_t c_rows_per_batch; int32_t c_row_offset; int32_t ldc;
+    const float *pos; int32_t pos_rows;   /* CONV2 only: fp32 [pos_rows][N]     */
+    uint16_t *q; uint16_t *k; uint16_t *vt; int32_t T; int32_t n_head; int32_t ldvt; float q_scale;
+    int32_t M, N, K;
+    int32_t epilogue;
+} wenc_gemm_args;
+int wenc_k_gemm(const wenc_gemm_args *args, void *stream);
+
+/* Non-causal attention per (batch, head) (kernels.nu, wk_attn with causal 0):
+ *   ao[b][t][h*64 + e] = sum_u softmax_u(q[b][h][t] . k[b][h][u]) * vt[b][h][e][u]
+ * with q ALREADY scaled by log2(e)/sqrt(64) (the softmax is taken in base 2),
+ * q, k fp16 [batch][n_head][T][64], vt fp16 [batch][n_head][64][ldvt],
+ * ao fp16 [batch][T][n_head*64].  ldvt % 8 == 0, ldvt >= T. */
+int wenc_k_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, uint16_t *ao,
+                     int32_t batch, int32_t n_head, int32_t T, int32_t ldvt, void *stream);
+
+/* Per-launch timing of wenc_forward with HIP events recorded on the caller's
+ * stream around the launches whose site bit is set in `site_mask`
+ * (bit s = 1 << WENC_SITE_*); 0 turns it off.  Events are read, and cleared,
+ * by wenc_profile_read (which synchronises on them). */
+enum {
+    WENC_SITE_INGEST = 0, WENC_SITE_CONV1 = 1, WENC_SITE_CONV2 = 2, WENC_SITE_LN1 = 3,
+    WENC_SITE_QKV = 4, WENC_SITE_ATTN = 5, WENC_SITE_OPROJ = 6, WENC_SITE_LN2 = 7,
+    WENC_SITE_FC1 = 8, WENC_SITE_FC2 = 9, WENC_SITE_LNF = 10, WENC_N_SITES = 11
+};
+int wenc_profile(wenc_t *h, uint32_t site_mask);
+/* ms_total[s] and launches[s] for s < WENC_N_SITES (arrays of that length). */
+int wenc_profile_read(wenc_t *h, double *ms_total, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WENC_H */

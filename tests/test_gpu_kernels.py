@@ -1,0 +1,238 @@
+"""Kernel parity on the GPU: each HIP kernel through its C-ABI entry point
+against the fp64 oracle, on seeded inputs spanning several tiles and a
+ragged tail.
+
+Tolerances follow from the arithmetic (fp16 operands are exact in both
+paths; the kernels accumulate in fp32):
+* fp16 outputs: one rounding, |err| <= 2^-11 |ref| (+ fp32 accumulation,
+  ~K 2^-24 sum|a w|): rtol 1e-3, atol 1e-4.
+* fp32 outputs: accumulation order only: rtol 1e-5, atol 1e-4.
+* attention: the probabilities are rounded to fp16 before P.V, so
+  |err| <= 2^-11 max|v| per output plus the output rounding: atol
+  1.5e-3 max|v|.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import DEV, dev, f16_dev, host, say
+from whisper_audio_encoder_amd import wenc
+
+pytestmark = pytest.mark.gpu
+
+LOG2E = 1.4426950408889634
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# ----------------------------------------------------------------- LayerNorm
+@pytest.mark.parametrize("rows,d", [(1, 384), (7, 512), (1001, 768), (333, 1280), (5, 4), (9, 260), (64, 2048)])
+@pytest.mark.parametrize("out_f32", [0, 1])
+def test_layernorm(rows, d, out_f32):
+    say(f"layernorm rows={rows} d={d} out_f32={out_f32}")
+    rng = np.random.default_rng(rows * 7 + d)
+    x = (rng.standard_normal((rows, d)) * rng.uniform(0.2, 3, (rows, 1)) + rng.uniform(-1, 1, (rows, 1))).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(d)).astype(np.float32)
+    y = torch.empty((rows, d), dtype=torch.float32 if out_f32 else torch.float16, device=DEV)
+    wenc.wenc_k_layernorm(dev(x), dev(g), dev(b), y, rows, d, 1e-5, out_f32)
+    ref = oracle.layer_norm(x, g, b, 1e-5)
+    got = host(y).astype(np.float64)
+    if out_f32:
+        np.testing.assert_allclose(got, ref, rtol=1e-5, atol=2e-5)
+    else:
+        np.testing.assert_allclose(got, ref, rtol=1e-3, atol=1e-4)
+
+
+def test_layernorm_empty():
+    wenc.wenc_k_layernorm(None, None, None, None, 0, 384, 1e-5, 0)
+
+
+# --------------------------------------------------------------------- GEMM
+def _gemm(A, W, bias, epi, M, N, K, **kw):
+    a = wenc.wenc_gemm_args()
+    a.A, a.W, a.bias = A.data_ptr(), W.data_ptr(), bias.data_ptr()
+    a.a_batch_stride = kw.get("a_batch_stride", 0)
+    a.a_rows_per_batch = kw.get("a_rows_per_batch", max(M, 1))
+    a.lda = kw.get("lda", K)
+    a.ldw = kw.get("ldw", K)
+    C = kw.get("C")
+    a.C = C.data_ptr() if C is not None else None
+    a.c_batch_stride = kw.get("c_batch_stride", 0)
+    a.c_rows_per_batch = kw.get("c_rows_per_batch", max(M, 1))
+    a.c_row_offset = kw.get("c_row_offset", 0)
+    a.ldc = kw.get("ldc", N)
+    pos = kw.get("pos")
+    a.pos = pos.data_ptr() if pos is not None else None
+    a.pos_rows = kw.get("pos_rows", 0)
+    for f in ("q", "k", "vt"):
+        t = kw.get(f)
+        setattr(a, f, t.data_ptr() if t is not None else None)
+    a.T = kw.get("T", 0)
+    a.n_head = kw.get("n_head", 0)
+    a.ldvt = kw.get("ldvt", 0)
+    a.q_scale = kw.get("q_scale", 1.0)
+    a.M, a.N, a.K, a.epilogue = M, N, K, epi
+    wenc.wenc_k_gemm(a)
+
+
+def _operands(rng, M, N, K):
+    A = rng.standard_normal((M, K)).astype(np.float16)
+    W = (0.05 * rng.standard_normal((N, K))).astype(np.float16)
+    b = (0.1 * rng.standard_normal(N)).astype(np.float32)
+    return A, W, b
+
+
+# (M, N, K): ragged M, N spanning several 128-wide tiles, K tails (240 = 3.75 steps of 64),
+# and shapes large enough for the 256 x 256 tile configuration.
+SHAPES = [(300, 384, 240), (1, 128, 8), (129, 640, 64), (1500, 1152, 384), (8192, 4096, 512), (24000, 768, 3072)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_resid(M, N, K):
+    say(f"gemm resid M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    A, W, b = _operands(rng, M, N, K)
+    x0 = rng.standard_normal((M, N)).astype(np.float32)
+    C = dev(x0)
+    _gemm(f16_dev(A), f16_dev(W), dev(b), wenc.WENC_EPI_RESID, M, N, K, C=C)
+    rows = np.unique(np.r_[np.arange(min(M, 64)), rng.integers(0, M, 256), M - 1])
+    ref = x0[rows] + _f64(A[rows]) @ _f64(W).T + b
+    np.testing.assert_allclose(host(C)[rows], ref, rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_gelu_f16(M, N, K):
+    say(f"gemm gelu M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 3 + N + K)
+    A, W, b = _operands(rng, M, N, K)
+    C = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    _gemm(f16_dev(A), f16_dev(W), dev(b), wenc.WENC_EPI_GELU_F16, M, N, K, C=C)
+    rows = np.unique(np.r_[np.arange(min(M, 64)), rng.integers(0, M, 256), M - 1])
+    ref = oracle.gelu(_f64(A[rows]) @ _f64(W).T + b)
+    np.testing.assert_allclose(host(C)[rows].astype(np.float64), ref, rtol=1e-3, atol=1e-4)
+
+
+def test_gemm_empty_m():
+    z = torch.zeros(64, dtype=torch.float16, device=DEV)
+    _gemm(z, z, torch.zeros(8, device=DEV), wenc.WENC_EPI_RESID, 0, 8, 8, C=z)
+
+
+@pytest.mark.parametrize("B,T,H,K", [(3, 100, 2, 128), (2, 1500, 6, 384), (1, 7, 1, 64)])
+def test_gemm_qkv_scatter(B, T, H, K):
+    say(f"gemm qkv B={B} T={T} H={H} K={K}")
+    rng = np.random.default_rng(B * T + H)
+    d = 64 * H
+    M, N = B * T, 3 * d
+    A, W, b = _operands(rng, M, N, K)
+    b[d:2 * d] = 0  # k_proj has no bias
+    ldvt = (T + 7) // 8 * 8
+    q = torch.empty((B, H, T, 64), dtype=torch.float16, device=DEV)
+    k = torch.empty_like(q)
+    vt = torch.zeros((B, H, 64, ldvt), dtype=torch.float16, device=DEV)
+    scale = LOG2E / 8
+    _gemm(f16_dev(A), f16_dev(W), dev(b), wenc.WENC_EPI_QKV, M, N, K, q=q, k=k, vt=vt, T=T, n_head=H,
+          ldvt=ldvt, q_scale=scale)
+    full = _f64(A) @ _f64(W).T + b  # [M, 3d]
+    ref_q = (full[:, :d] * scale).reshape(B, T, H, 64).transpose(0, 2, 1, 3)
+    ref_k = full[:, d:2 * d].reshape(B, T, H, 64).transpose(0, 2, 1, 3)
+    ref_v = full[:, 2 * d:].reshape(B, T, H, 64).transpose(0, 2, 3, 1)
+    np.testing.assert_allclose(host(q).astype(np.float64), ref_q, rtol=1e-3, atol=1e-4)
+    np.testing.assert_allclose(host(k).astype(np.float64), ref_k, rtol=1e-3, atol=1e-4)
+    np.testing.assert_allclose(host(vt)[..., :T].astype(np.float64), ref_v, rtol=1e-3, atol=1e-4)
+
+
+@pytest.mark.parametrize("B,F,C,O", [(2, 32, 16, 64), (3, 3000, 80, 384), (1, 10, 8, 128)])
+def test_gemm_conv_stem(B, F, C, O):
+    """conv1 (stride 1) and conv2 (stride 2) as GEMMs over overlapping frame
+    windows of zero-padded, frame-contiguous buffers, against oracle.conv1d."""
+    say(f"gemm conv stem B={B} F={F} C={C} O={O}")
+    rng = np.random.default_rng(F + C + O)
+    mel = rng.standard_normal((B, F, C)).astype(np.float32)
+    melp = np.zeros((B, F + 2, C), dtype=np.float16)
+    melp[:, 1:F + 1] = mel.astype(np.float16)
+    w1 = (0.05 * rng.standard_normal((O, C, 3))).astype(np.float16)
+    b1 = (0.1 * rng.standard_normal(O)).astype(np.float32)
+    w2 = (0.05 * rng.standard_normal((O, O, 3))).astype(np.float16)
+    b2 = (0.1 * rng.standard_normal(O)).astype(np.float32)
+    T = F // 2
+    pos = rng.standard_normal((T, O)).astype(np.float32)
+    pk = lambda w: np.ascontiguousarray(w.transpose(0, 2, 1).reshape(w.shape[0], -1))  # [out][k][in]
+    c1 = torch.full((B, F + 2, O), float("nan"), dtype=torch.float16, device=DEV)
+    c1[:, 0] = 0
+    c1[:, F + 1] = 0
+    _gemm(f16_dev(melp), f16_dev(pk(w1)), dev(b1), wenc.WENC_EPI_GELU_F16, B * F, O, 3 * C,
+          a_batch_stride=(F + 2) * C, a_rows_per_batch=F, lda=C, C=c1, c_batch_stride=(F + 2) * O,
+          c_rows_per_batch=F, c_row_offset=1, ldc=O)
+    x = torch.full((B * T, O), float("nan"), dtype=torch.float32, device=DEV)
+    _gemm(c1, f16_dev(pk(w2)), dev(b2), wenc.WENC_EPI_CONV2, B * T, O, 3 * O,
+          a_batch_stride=(F + 2) * O, a_rows_per_batch=T, lda=2 * O, C=x, pos=dev(pos), pos_rows=T)
+    c1h = host(c1).astype(np.float64)
+    xh = host(x).reshape(B, T, O)
+    for bi in range(B):
+        ref1 = oracle.gelu(oracle.conv1d(melp[bi, 1:F + 1], w1, b1, stride=1))
+        np.testing.assert_allclose(c1h[bi, 1:F + 1], ref1, rtol=1e-3, atol=1e-4)
+        # conv2 consumes the GPU's own fp16 conv1 output (so only conv2 is tested here)
+        ref2 = oracle.gelu(oracle.conv1d(c1h[bi, 1:F + 1], w2, b2, stride=2)) + pos
+        np.testing.assert_allclose(xh[bi], ref2, rtol=1e-5, atol=1e-4)
+
+
+# ----------------------------------------------------------------- attention
+def _attention_case(rng, B, H, T, mode):
+    if mode == "random":
+        q = rng.standard_normal((B, H, T, 64))
+        k = rng.standard_normal((B, H, T, 64))
+    elif mode == "sharp":  # score std ~5 in log2 units
+        q = 0.8 * rng.standard_normal((B, H, T, 64))
+        k = 0.8 * rng.standard_normal((B, H, T, 64))
+    else:  # "dominant": one key per query ~60 log2 units above the rest, anywhere in the sequence
+        k = rng.standard_normal((B, H, T, 64))
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        tgt = rng.integers(0, T, (B, H, T))
+        q = np.take_along_axis(k, tgt[..., None], axis=2) * 60.0 + 0.3 * rng.standard_normal((B, H, T, 64))
+    v = rng.standard_normal((B, H, T, 64))
+    return q, k, v
+
+
+@pytest.mark.parametrize("T", [1, 50, 64, 65, 129, 1500])
+@pytest.mark.parametrize("mode", ["random", "sharp", "dominant"])
+def test_attention(T, mode):
+    B, H = 2, 3
+    say(f"attention T={T} mode={mode}")
+    rng = np.random.default_rng(T * 11 + len(mode))
+    q, k, v = _attention_case(rng, B, H, T, mode)
+    # the kernel takes q in log2 units (times log2(e)/8); dominant mode builds it that way directly
+    qk = (q if mode == "dominant" else q * (LOG2E / 8)).astype(np.float16)
+    kh = k.astype(np.float16)
+    vh = v.astype(np.float16)
+    ldvt = (T + 7) // 8 * 8
+    vt = np.zeros((B, H, 64, ldvt), dtype=np.float16)
+    vt[..., :T] = vh.transpose(0, 1, 3, 2)
+    ao = torch.full((B, T, H * 64), float("nan"), dtype=torch.float16, device=DEV)
+    wenc.wenc_k_attention(f16_dev(qk), f16_dev(kh), f16_dev(vt), ao, B, H, T, ldvt)
+    got = host(ao).astype(np.float64).reshape(B, T, H, 64)
+    q_eff = _f64(qk) * (8 * math.log(2))  # scores q_eff.k/8 = (qk.k) ln 2: base-2 softmax of qk.k
+    for bi in range(B):
+        for h in range(H):
+            ref = oracle.attention(q_eff[bi, h], _f64(kh[bi, h]), _f64(vh[bi, h]))
+            np.testing.assert_allclose(got[bi, :, h], ref, rtol=0, atol=1.5e-3 * np.abs(vh).max())
+
+
+def test_attention_poisoned_vt_padding():
+    """V^T columns between T and ldvt may hold anything (NaN here)."""
+    B, H, T = 1, 2, 61
+    say("attention NaN padding")
+    rng = np.random.default_rng(5)
+    q, k, v = _attention_case(rng, B, H, T, "random")
+    ldvt = 64
+    vt = np.full((B, H, 64, ldvt), np.nan, dtype=np.float16)
+    vt[..., :T] = v.astype(np.float16).transpose(0, 1, 3, 2)
+    qk = (q * (LOG2E / 8)).astype(np.float16)
+    ao = torch.empty((B, T, H * 64), dtype=torch.float16, device=DEV)
+    wenc.wenc_k_attention(f16_dev(qk), f16_dev(k.astype(np.float16)), f16_dev(vt), ao, B, H, T, ldvt)
+    assert np.isfinite(host(ao)).all()

@@ -1,0 +1,27 @@
+// Host-side launchers of the gfx950 kernels (internal to libwenc.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include "wenc.h"
+
+namespace wk {
+
+// Checks the shape/alignment contract of wenc_gemm_args; returns a message
+// or nullptr when the arguments are acceptable.
+const char *gemm_check(const wenc_gemm_args &a);
+hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s);
+
+const char *attention_check(int batch, int n_head, int T, int ldvt);
+hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, uint16_t *ao,
+                            int batch, int n_head, int T, int ldvt, hipStream_t s);
+
+const char *layernorm_check(int rows, int d);
+hipError_t launch_layernorm(const float *x, const float *g, const float *b, void *y, int rows, int d,
+                            float eps, bool out_f32, hipStream_t s);
+
+// mel fp32 [B][F][nm] -> melp fp16 [B][F+2][nm] with zero first/last frame,
+// and zero rows 0 and F+1 of c1 fp16 [B][F+2][d].
+hipError_t launch_ingest(const float *mel, uint16_t *melp, uint16_t *c1, int B, int F, int nm, int d,
+                         hipStream_t s);
+
+}  // namespace wk

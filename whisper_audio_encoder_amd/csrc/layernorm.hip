@@ -1,0 +1,154 @@
+// LayerNorm (with bias) and mel ingest, for gfx950.  Both are bound by HBM
+// bandwidth: each row is read once and written once with 16-byte loads.
+//
+// LayerNorm (whisper 0.9.0 API page, kernels.nu: it subtracts the mean and
+// has a bias, unlike RMSNorm): one wave64 per row, the row held in registers
+// (float4 per lane per 256 columns), two passes over those registers for
+// the mean and the population variance, wave reductions by lane exchange.
+#include "common.h"
+#include "kernels.h"
+
+namespace wk {
+
+namespace {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+template <int NV, bool OUT32>
+__global__ void __launch_bounds__(256)
+ln_kernel(const float *__restrict__ x, const float *__restrict__ g, const float *__restrict__ bta,
+          void *__restrict__ y, int rows, int d, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int nv = d >> 2;
+    const float4 *xr = reinterpret_cast<const float4 *>(x + int64_t(row) * d);
+    float4 v[NV];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = lane + 64 * j;
+        if (i < nv) {
+            v[j] = xr[i];
+            s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+        } else {
+            v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    const float mean = wave_sum(s) / float(d);
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = lane + 64 * j;
+        if (i < nv) {
+            const float a = v[j].x - mean, b = v[j].y - mean, c = v[j].z - mean, e = v[j].w - mean;
+            ss += (a * a + b * b) + (c * c + e * e);
+        }
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(ss) / float(d) + eps);
+    const float4 *g4 = reinterpret_cast<const float4 *>(g);
+    const float4 *b4 = reinterpret_cast<const float4 *>(bta);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = lane + 64 * j;
+        if (i < nv) {
+            const float4 gg = g4[i], bb = b4[i];
+            const float o0 = (v[j].x - mean) * rstd * gg.x + bb.x;
+            const float o1 = (v[j].y - mean) * rstd * gg.y + bb.y;
+            const float o2 = (v[j].z - mean) * rstd * gg.z + bb.z;
+            const float o3 = (v[j].w - mean) * rstd * gg.w + bb.w;
+            if constexpr (OUT32) {
+                reinterpret_cast<float4 *>(static_cast<float *>(y) + int64_t(row) * d)[i] = make_float4(o0, o1, o2, o3);
+            } else {
+                f16x4 w = {(f16)o0, (f16)o1, (f16)o2, (f16)o3};
+                reinterpret_cast<f16x4 *>(static_cast<f16 *>(y) + int64_t(row) * d)[i] = w;
+            }
+        }
+    }
+}
+
+template <int NV>
+hipError_t ln_dispatch(const float *x, const float *g, const float *b, void *y, int rows, int d, float eps,
+                       bool out_f32, hipStream_t s) {
+    const dim3 grid((rows + 3) / 4), block(256);
+    if (out_f32)
+        ln_kernel<NV, true><<<grid, block, 0, s>>>(x, g, b, y, rows, d, eps);
+    else
+        ln_kernel<NV, false><<<grid, block, 0, s>>>(x, g, b, y, rows, d, eps);
+    return hipGetLastError();
+}
+
+// melp[b][r][c] = r in [1, F] ? fp16(mel[b][r-1][c]) : 0, four values per
+// thread; then rows 0 and F+1 of c1[b] are cleared.
+__global__ void __launch_bounds__(256)
+ingest_kernel(const float *__restrict__ mel, f16 *__restrict__ melp, f16 *__restrict__ c1, int B, int F, int nm,
+              int d) {
+    const int64_t n1 = int64_t(B) * (F + 2) * (nm >> 2);
+    const int64_t n2 = int64_t(B) * 2 * (d >> 2);
+    const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n1 + n2; i += stride) {
+        if (i < n1) {
+            const int64_t per_item = int64_t(F + 2) * (nm >> 2);
+            const int64_t b = i / per_item;
+            const int64_t rem = i - b * per_item;
+            const int r = int(rem / (nm >> 2));
+            const int c4 = int(rem - int64_t(r) * (nm >> 2));
+            f16x4 w = {0, 0, 0, 0};
+            if (r >= 1 && r <= F) {
+                const float4 v = reinterpret_cast<const float4 *>(mel + (b * F + (r - 1)) * nm)[c4];
+                w = f16x4{(f16)v.x, (f16)v.y, (f16)v.z, (f16)v.w};
+            }
+            reinterpret_cast<f16x4 *>(melp + (b * (F + 2) + r) * nm)[c4] = w;
+        } else {
+            const int64_t j = i - n1;
+            const int64_t per_item = 2 * (d >> 2);
+            const int64_t b = j / per_item;
+            const int64_t rem = j - b * per_item;
+            const int which = int(rem / (d >> 2));
+            const int c4 = int(rem - int64_t(which) * (d >> 2));
+            const int64_t row = b * (F + 2) + (which ? F + 1 : 0);
+            reinterpret_cast<f16x4 *>(c1 + row * d)[c4] = f16x4{0, 0, 0, 0};
+        }
+    }
+}
+
+}  // namespace
+
+const char *layernorm_check(int rows, int d) {
+    if (rows < 0) return "layernorm: rows < 0";
+    if (d <= 0 || d % 4 || d > 2048) return "layernorm: need 0 < d <= 2048 and d % 4 == 0";
+    return nullptr;
+}
+
+hipError_t launch_layernorm(const float *x, const float *g, const float *b, void *y, int rows, int d, float eps,
+                            bool out_f32, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    const int nv = (d / 4 + 63) / 64;
+    switch (nv) {
+        case 1: return ln_dispatch<1>(x, g, b, y, rows, d, eps, out_f32, s);
+        case 2: return ln_dispatch<2>(x, g, b, y, rows, d, eps, out_f32, s);
+        case 3: return ln_dispatch<3>(x, g, b, y, rows, d, eps, out_f32, s);
+        case 4: return ln_dispatch<4>(x, g, b, y, rows, d, eps, out_f32, s);
+        case 5: return ln_dispatch<5>(x, g, b, y, rows, d, eps, out_f32, s);
+        case 6: return ln_dispatch<6>(x, g, b, y, rows, d, eps, out_f32, s);
+        case 7: return ln_dispatch<7>(x, g, b, y, rows, d, eps, out_f32, s);
+        case 8: return ln_dispatch<8>(x, g, b, y, rows, d, eps, out_f32, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_ingest(const float *mel, uint16_t *melp, uint16_t *c1, int B, int F, int nm, int d, hipStream_t s) {
+    if (B == 0) return hipSuccess;
+    const int64_t n = int64_t(B) * (F + 2) * (nm / 4) + int64_t(B) * 2 * (d / 4);
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    ingest_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, s>>>(mel, reinterpret_cast<f16 *>(melp),
+                                                             reinterpret_cast<f16 *>(c1), B, F, nm, d);
+    return hipGetLastError();
+}
+
+}  // namespace wk

@@ -1,0 +1,609 @@
+// Host runtime of libwenc.so: the C ABI declared in include/wenc.h.
+//
+// Owns one device arena for the repacked weights (one upload per load, as
+// the whisper README's memory notes describe: the checkpoint is mapped,
+// uploaded once and released) and one arena for the activations of
+// max_batch windows.  wenc_forward only enqueues kernels on the caller's
+// stream: ingest, conv1, conv2, then per block LN1, QKV, attention,
+// out_proj, LN2, fc1, fc2, and the final LN (3 + 7 L + 1 launches per chunk).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "wenc.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(std::string *dst, int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (dst) *dst = buf;
+    g_err = buf;
+    return code;
+}
+
+// IEEE binary16 -> binary32, exact (subnormals, infinities and NaN included).
+float half_to_float(uint16_t h) {
+    const uint32_t sign = uint32_t(h & 0x8000u) << 16;
+    uint32_t exp = (h >> 10) & 0x1f;
+    uint32_t man = h & 0x3ffu;
+    uint32_t bits;
+    if (exp == 0) {
+        if (man == 0) {
+            bits = sign;
+        } else {
+            exp = 127 - 15 + 1;
+            while (!(man & 0x400u)) {
+                man <<= 1;
+                --exp;
+            }
+            man &= 0x3ffu;
+            bits = sign | (exp << 23) | (man << 13);
+        }
+    } else if (exp == 31) {
+        bits = sign | 0x7f800000u | (man << 13);
+    } else {
+        bits = sign | ((exp + 127 - 15) << 23) | (man << 13);
+    }
+    float f;
+    std::memcpy(&f, &bits, 4);
+    return f;
+}
+
+struct Bump {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        const size_t o = (off + 255) & ~size_t(255);
+        off = o + bytes;
+        return o;
+    }
+};
+
+struct LayerOff {
+    size_t ln1_g, ln1_b, wqkv, bqkv, wo, bo, ln2_g, ln2_b, fc1_w, fc1_b, fc2_w, fc2_b;
+};
+
+struct WeightLayout {
+    size_t conv1_w, conv1_b, conv2_w, conv2_b, pos, lnf_g, lnf_b;
+    std::vector<LayerOff> layers;
+    size_t total;
+};
+
+WeightLayout weight_layout(const wenc_config &c) {
+    const size_t d = c.d_model, F = c.d_ff, nm = c.n_mels, T = c.n_ctx;
+    WeightLayout w;
+    Bump b;
+    w.conv1_w = b.take(2 * d * 3 * nm);
+    w.conv1_b = b.take(4 * d);
+    w.conv2_w = b.take(2 * d * 3 * d);
+    w.conv2_b = b.take(4 * d);
+    w.pos = b.take(4 * T * d);
+    for (int l = 0; l < c.n_layer; ++l) {
+        LayerOff o;
+        o.ln1_g = b.take(4 * d);
+        o.ln1_b = b.take(4 * d);
+        o.wqkv = b.take(2 * 3 * d * d);
+        o.bqkv = b.take(4 * 3 * d);
+        o.wo = b.take(2 * d * d);
+        o.bo = b.take(4 * d);
+        o.ln2_g = b.take(4 * d);
+        o.ln2_b = b.take(4 * d);
+        o.fc1_w = b.take(2 * F * d);
+        o.fc1_b = b.take(4 * F);
+        o.fc2_w = b.take(2 * d * F);
+        o.fc2_b = b.take(4 * d);
+        w.layers.push_back(o);
+    }
+    w.lnf_g = b.take(4 * d);
+    w.lnf_b = b.take(4 * d);
+    w.total = (b.off + 255) & ~size_t(255);
+    return w;
+}
+
+struct ScratchLayout {
+    size_t melp, c1, x, xn, q, k, vt, ao, hbuf, total;
+    int ldvt;
+};
+
+ScratchLayout scratch_layout(const wenc_config &c) {
+    const size_t B = c.max_batch, F = c.n_frames, nm = c.n_mels, d = c.d_model, T = c.n_ctx, H = c.n_head,
+                 Fd = c.d_ff;
+    ScratchLayout s;
+    s.ldvt = int((T + 7) / 8 * 8);
+    Bump b;
+    s.melp = b.take(2 * B * (F + 2) * nm);
+    s.c1 = b.take(2 * B * (F + 2) * d);
+    s.x = b.take(4 * B * T * d);
+    s.xn = b.take(2 * B * T * d);
+    s.q = b.take(2 * B * H * T * 64);
+    s.k = b.take(2 * B * H * T * 64);
+    s.vt = b.take(2 * B * H * 64 * size_t(s.ldvt));
+    s.ao = b.take(2 * B * T * d);
+    s.hbuf = b.take(2 * B * T * Fd);
+    s.total = (b.off + 255) & ~size_t(255);
+    return s;
+}
+
+const char *config_error(const wenc_config *c) {
+    if (!c) return "config is NULL";
+    if (c->head_dim != 64) return "head_dim must be 64";
+    if (c->n_head <= 0 || c->d_model != c->n_head * 64) return "d_model must equal n_head * 64 with n_head > 0";
+    if (c->d_model > 2048) return "d_model must be <= 2048";
+    if (c->n_mels <= 0 || c->n_mels % 8 || c->n_mels > 4096) return "n_mels must be a positive multiple of 8, <= 4096";
+    if (c->d_ff <= 0 || c->d_ff % 8 || c->d_ff > 65536) return "d_ff must be a positive multiple of 8, <= 65536";
+    if (c->n_layer < 0 || c->n_layer > 4096) return "n_layer must be in [0, 4096]";
+    if (c->n_ctx <= 0 || c->n_ctx >= 32768 || c->n_frames != 2 * c->n_ctx)
+        return "n_frames must equal 2 * n_ctx with 0 < n_ctx < 32768";
+    if (!(c->ln_eps > 0.f) || !std::isfinite(c->ln_eps)) return "ln_eps must be positive and finite";
+    if (c->final_ln != 0 && c->final_ln != 1) return "final_ln must be 0 or 1";
+    if (c->max_batch < 1) return "max_batch must be >= 1";
+    if (int64_t(c->max_batch) * c->n_frames >= (int64_t(1) << 24)) return "max_batch * n_frames must be < 2^24";
+    return nullptr;
+}
+
+size_t blob_halves(const wenc_config &c) {
+    const size_t d = c.d_model, F = c.d_ff, nm = c.n_mels, T = c.n_ctx;
+    const size_t layer = 2 * d + 4 * d * d + 2 * d + d + 2 * d + F * d + F + d * F + d;
+    return d * nm * 3 + d + d * d * 3 + d + T * d + c.n_layer * layer + 2 * d;
+}
+
+struct ProfRec {
+    int site;
+    hipEvent_t e0, e1;
+};
+
+}  // namespace
+
+struct wenc {
+    wenc_config cfg;
+    int device = 0;
+    char *warena = nullptr;
+    char *sarena = nullptr;
+    WeightLayout wl;
+    ScratchLayout sl;
+    bool loaded = false;
+    bool debug_sync = false;
+    std::string err;
+    uint32_t prof_mask = 0;
+    std::vector<ProfRec> prof_pending;
+    std::vector<hipEvent_t> event_pool;
+
+    template <class T>
+    T *W(size_t off) const { return reinterpret_cast<T *>(warena + off); }
+    template <class T>
+    T *S(size_t off) const { return reinterpret_cast<T *>(sarena + off); }
+
+    hipEvent_t take_event() {
+        if (!event_pool.empty()) {
+            hipEvent_t e = event_pool.back();
+            event_pool.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+
+    // Launch one site, optionally bracketed by timing events.
+    template <class Fn>
+    int site(int s, hipStream_t st, Fn &&launch) {
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        const bool prof = (prof_mask >> s) & 1u;
+        if (prof) {
+            e0 = take_event();
+            e1 = take_event();
+            if (!e0 || !e1) return fail(&err, WENC_EHIP, "hipEventCreate failed");
+            const hipError_t er = hipEventRecord(e0, st);
+            if (er != hipSuccess) return fail(&err, WENC_EHIP, "hipEventRecord: %s", hipGetErrorString(er));
+        }
+        hipError_t e = launch();
+        if (prof) {
+            const hipError_t er = hipEventRecord(e1, st);
+            prof_pending.push_back({s, e0, e1});
+            if (er != hipSuccess) return fail(&err, WENC_EHIP, "hipEventRecord: %s", hipGetErrorString(er));
+        }
+        if (e != hipSuccess) return fail(&err, WENC_EHIP, "launch at site %d failed: %s", s, hipGetErrorString(e));
+        if (debug_sync) {
+            e = hipStreamSynchronize(st);
+            if (e == hipSuccess) e = hipGetLastError();
+            if (e != hipSuccess) return fail(&err, WENC_EHIP, "site %d failed at sync: %s", s, hipGetErrorString(e));
+        }
+        return WENC_OK;
+    }
+
+    int forward_chunk(const float *mel, int nb, float *out, hipStream_t st, int tap, void *tap_dst);
+};
+
+#define WENC_TRY(expr)                 \
+    do {                               \
+        const int rc_ = (expr);        \
+        if (rc_ != WENC_OK) return rc_; \
+    } while (0)
+
+int wenc::forward_chunk(const float *mel, int nb, float *out, hipStream_t st, int tap, void *tap_dst) {
+    const wenc_config &c = cfg;
+    const int F = c.n_frames, T = c.n_ctx, nm = c.n_mels, d = c.d_model, H = c.n_head, Fd = c.d_ff;
+    const int M = nb * T;
+    uint16_t *melp = S<uint16_t>(sl.melp), *c1 = S<uint16_t>(sl.c1), *xn = S<uint16_t>(sl.xn);
+    uint16_t *q = S<uint16_t>(sl.q), *k = S<uint16_t>(sl.k), *vt = S<uint16_t>(sl.vt);
+    uint16_t *ao = S<uint16_t>(sl.ao), *hb = S<uint16_t>(sl.hbuf);
+    float *x = S<float>(sl.x);
+
+    WENC_TRY(site(WENC_SITE_INGEST, st, [&] { return wk::launch_ingest(mel, melp, c1, nb, F, nm, d, st); }));
+
+    wenc_gemm_args g{};
+    // conv1: output frame t reads padded frames t .. t+2 (3 n_mels contiguous values).
+    g.A = melp;
+    g.a_batch_stride = int64_t(F + 2) * nm;
+    g.a_rows_per_batch = F;
+    g.lda = nm;
+    g.W = W<uint16_t>(wl.conv1_w);
+    g.ldw = 3 * nm;
+    g.bias = W<float>(wl.conv1_b);
+    g.C = c1;
+    g.c_batch_stride = int64_t(F + 2) * d;
+    g.c_rows_per_batch = F;
+    g.c_row_offset = 1;
+    g.ldc = d;
+    g.M = nb * F;
+    g.N = d;
+    g.K = 3 * nm;
+    g.epilogue = WENC_EPI_GELU_F16;
+    WENC_TRY(site(WENC_SITE_CONV1, st, [&] { return wk::launch_gemm(g, st); }));
+    if (tap == WENC_TAP_C1) {
+        const hipError_t e = hipMemcpy2DAsync(tap_dst, size_t(F) * d * 2, c1 + d, size_t(F + 2) * d * 2,
+                                              size_t(F) * d * 2, nb, hipMemcpyDeviceToDevice, st);
+        return e == hipSuccess ? WENC_OK : fail(&err, WENC_EHIP, "tap copy: %s", hipGetErrorString(e));
+    }
+
+    // conv2: output position t reads padded conv1 rows 2t .. 2t+2.
+    g = wenc_gemm_args{};
+    g.A = c1;
+    g.a_batch_stride = int64_t(F + 2) * d;
+    g.a_rows_per_batch = T;
+    g.lda = 2 * d;
+    g.W = W<uint16_t>(wl.conv2_w);
+    g.ldw = 3 * d;
+    g.bias = W<float>(wl.conv2_b);
+    g.C = x;
+    g.ldc = d;
+    g.pos = W<float>(wl.pos);
+    g.pos_rows = T;
+    g.M = M;
+    g.N = d;
+    g.K = 3 * d;
+    g.epilogue = WENC_EPI_CONV2;
+    WENC_TRY(site(WENC_SITE_CONV2, st, [&] { return wk::launch_gemm(g, st); }));
+    auto copy_x = [&](void *dst) {
+        const hipError_t e = hipMemcpyAsync(dst, x, size_t(M) * d * 4, hipMemcpyDeviceToDevice, st);
+        return e == hipSuccess ? WENC_OK : fail(&err, WENC_EHIP, "tap copy: %s", hipGetErrorString(e));
+    };
+    if (tap == WENC_TAP_STEM) return copy_x(tap_dst);
+
+    const float q_scale = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
+    for (int l = 0; l < c.n_layer; ++l) {
+        const LayerOff &lo = wl.layers[l];
+        WENC_TRY(site(WENC_SITE_LN1, st, [&] {
+            return wk::launch_layernorm(x, W<float>(lo.ln1_g), W<float>(lo.ln1_b), xn, M, d, c.ln_eps, false, st);
+        }));
+        g = wenc_gemm_args{};
+        g.A = xn;
+        g.a_batch_stride = int64_t(T) * d;
+        g.a_rows_per_batch = T;
+        g.lda = d;
+        g.W = W<uint16_t>(lo.wqkv);
+        g.ldw = d;
+        g.bias = W<float>(lo.bqkv);
+        g.q = q;
+        g.k = k;
+        g.vt = vt;
+        g.T = T;
+        g.n_head = H;
+        g.ldvt = sl.ldvt;
+        g.q_scale = q_scale;
+        g.M = M;
+        g.N = 3 * d;
+        g.K = d;
+        g.epilogue = WENC_EPI_QKV;
+        WENC_TRY(site(WENC_SITE_QKV, st, [&] { return wk::launch_gemm(g, st); }));
+        WENC_TRY(site(WENC_SITE_ATTN, st, [&] { return wk::launch_attention(q, k, vt, ao, nb, H, T, sl.ldvt, st); }));
+        g = wenc_gemm_args{};
+        g.A = ao;
+        g.a_batch_stride = int64_t(T) * d;
+        g.a_rows_per_batch = T;
+        g.lda = d;
+        g.W = W<uint16_t>(lo.wo);
+        g.ldw = d;
+        g.bias = W<float>(lo.bo);
+        g.C = x;
+        g.ldc = d;
+        g.M = M;
+        g.N = d;
+        g.K = d;
+        g.epilogue = WENC_EPI_RESID;
+        WENC_TRY(site(WENC_SITE_OPROJ, st, [&] { return wk::launch_gemm(g, st); }));
+        WENC_TRY(site(WENC_SITE_LN2, st, [&] {
+            return wk::launch_layernorm(x, W<float>(lo.ln2_g), W<float>(lo.ln2_b), xn, M, d, c.ln_eps, false, st);
+        }));
+        g = wenc_gemm_args{};
+        g.A = xn;
+        g.a_batch_stride = int64_t(T) * d;
+        g.a_rows_per_batch = T;
+        g.lda = d;
+        g.W = W<uint16_t>(lo.fc1_w);
+        g.ldw = d;
+        g.bias = W<float>(lo.fc1_b);
+        g.C = hb;
+        g.c_batch_stride = int64_t(T) * Fd;
+        g.c_rows_per_batch = T;
+        g.ldc = Fd;
+        g.M = M;
+        g.N = Fd;
+        g.K = d;
+        g.epilogue = WENC_EPI_GELU_F16;
+        WENC_TRY(site(WENC_SITE_FC1, st, [&] { return wk::launch_gemm(g, st); }));
+        g = wenc_gemm_args{};
+        g.A = hb;
+        g.a_batch_stride = int64_t(T) * Fd;
+        g.a_rows_per_batch = T;
+        g.lda = Fd;
+        g.W = W<uint16_t>(lo.fc2_w);
+        g.ldw = Fd;
+        g.bias = W<float>(lo.fc2_b);
+        g.C = x;
+        g.ldc = d;
+        g.M = M;
+        g.N = d;
+        g.K = Fd;
+        g.epilogue = WENC_EPI_RESID;
+        WENC_TRY(site(WENC_SITE_FC2, st, [&] { return wk::launch_gemm(g, st); }));
+        if (tap == WENC_TAP_BLOCK + l) return copy_x(tap_dst);
+    }
+
+    if (c.final_ln) {
+        WENC_TRY(site(WENC_SITE_LNF, st, [&] {
+            return wk::launch_layernorm(x, W<float>(wl.lnf_g), W<float>(wl.lnf_b), out, M, d, c.ln_eps, true, st);
+        }));
+        return WENC_OK;
+    }
+    return copy_x(out);
+}
+
+extern "C" {
+
+size_t wenc_weights_nbytes(const wenc_config *cfg) {
+    if (config_error(cfg)) return 0;
+    return 2 * blob_halves(*cfg);
+}
+
+int wenc_create(const wenc_config *cfg, wenc_t **out) {
+    if (!out) return fail(nullptr, WENC_EINVAL, "wenc_create: out is NULL");
+    *out = nullptr;
+    if (const char *m = config_error(cfg)) return fail(nullptr, WENC_EINVAL, "wenc_create: %s", m);
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess || n <= 0)
+        return fail(nullptr, WENC_ENODEV, "wenc_create: no HIP device (%s)", e != hipSuccess ? hipGetErrorString(e) : "count 0");
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(nullptr, WENC_ENODEV, "wenc_create: hipGetDevice: %s", hipGetErrorString(e));
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(nullptr, WENC_ENODEV, "wenc_create: hipGetDeviceProperties: %s", hipGetErrorString(e));
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(nullptr, WENC_ENODEV, "wenc_create: device %d is %s; this library is built for gfx950", dev,
+                    prop.gcnArchName);
+
+    wenc *h = new wenc();
+    h->cfg = *cfg;
+    h->device = dev;
+    h->wl = weight_layout(*cfg);
+    h->sl = scratch_layout(*cfg);
+    const char *dbg = std::getenv("WENC_DEBUG_SYNC");
+    h->debug_sync = dbg && dbg[0] == '1';
+    auto alloc = [&](char **p, size_t bytes, const char *what) -> int {
+        const hipError_t ea = hipMalloc(reinterpret_cast<void **>(p), bytes);
+        if (ea != hipSuccess) {
+            (void)hipGetLastError();
+            size_t fr = 0, tot = 0;
+            hipMemGetInfo(&fr, &tot);
+            *p = nullptr;
+            return fail(nullptr, WENC_ENOMEM, "wenc_create: cannot allocate %zu bytes of %s (device has %zu free of %zu)",
+                        bytes, what, fr, tot);
+        }
+        return WENC_OK;
+    };
+    int rc = alloc(&h->warena, h->wl.total, "weights");
+    if (rc == WENC_OK) rc = alloc(&h->sarena, h->sl.total, "activation scratch");
+    if (rc == WENC_OK) {
+        // WENC_POISON_SCRATCH=1 fills the activations with all-ones bytes (NaN
+        // in fp16 and fp32) so that a read of never-written scratch shows up.
+        const char *poison = std::getenv("WENC_POISON_SCRATCH");
+        e = hipMemset(h->sarena, poison && poison[0] == '1' ? 0xff : 0, h->sl.total);
+        if (e != hipSuccess) rc = fail(nullptr, WENC_EHIP, "wenc_create: hipMemset: %s", hipGetErrorString(e));
+    }
+    if (rc != WENC_OK) {
+        if (h->warena) hipFree(h->warena);
+        if (h->sarena) hipFree(h->sarena);
+        delete h;
+        return rc;
+    }
+    *out = h;
+    return WENC_OK;
+}
+
+int wenc_load(wenc_t *h, const void *blob, size_t nbytes) {
+    if (!h) return fail(nullptr, WENC_EINVAL, "wenc_load: handle is NULL");
+    if (!blob) return fail(&h->err, WENC_EINVAL, "wenc_load: blob is NULL");
+    const wenc_config &c = h->cfg;
+    const size_t want = 2 * blob_halves(c);
+    if (nbytes != want)
+        return fail(&h->err, WENC_EINVAL, "wenc_load: blob has %zu bytes, this config needs exactly %zu", nbytes, want);
+    const size_t d = c.d_model, F = c.d_ff, nm = c.n_mels, T = c.n_ctx;
+    std::vector<char> host(h->wl.total, 0);
+    const uint16_t *src = static_cast<const uint16_t *>(blob);
+    auto f32 = [&](size_t off, size_t n) {
+        float *dst = reinterpret_cast<float *>(host.data() + off);
+        for (size_t i = 0; i < n; ++i) dst[i] = half_to_float(src[i]);
+        src += n;
+    };
+    auto f16 = [&](size_t off, size_t n) {
+        std::memcpy(host.data() + off, src, 2 * n);
+        src += n;
+    };
+    // conv taps [out][in][k] -> [out][k][in] so a GEMM row reads k-major windows.
+    auto conv = [&](size_t off, size_t cout, size_t cin) {
+        uint16_t *dst = reinterpret_cast<uint16_t *>(host.data() + off);
+        for (size_t o = 0; o < cout; ++o)
+            for (size_t ci = 0; ci < cin; ++ci)
+                for (size_t j = 0; j < 3; ++j) dst[o * 3 * cin + j * cin + ci] = src[(o * cin + ci) * 3 + j];
+        src += cout * cin * 3;
+    };
+    conv(h->wl.conv1_w, d, nm);
+    f32(h->wl.conv1_b, d);
+    conv(h->wl.conv2_w, d, d);
+    f32(h->wl.conv2_b, d);
+    f32(h->wl.pos, T * d);
+    for (int l = 0; l < c.n_layer; ++l) {
+        const LayerOff &lo = h->wl.layers[l];
+        f32(lo.ln1_g, d);
+        f32(lo.ln1_b, d);
+        f16(lo.wqkv, d * d);                 // wq -> rows [0, d)
+        f32(lo.bqkv, d);                     // bq
+        f16(lo.wqkv + 2 * d * d, d * d);     // wk -> rows [d, 2d); k_proj has no bias (left 0)
+        f16(lo.wqkv + 4 * d * d, d * d);     // wv -> rows [2d, 3d)
+        f32(lo.bqkv + 4 * 2 * d, d);         // bv
+        f16(lo.wo, d * d);
+        f32(lo.bo, d);
+        f32(lo.ln2_g, d);
+        f32(lo.ln2_b, d);
+        f16(lo.fc1_w, F * d);
+        f32(lo.fc1_b, F);
+        f16(lo.fc2_w, d * F);
+        f32(lo.fc2_b, d);
+    }
+    f32(h->wl.lnf_g, d);
+    f32(h->wl.lnf_b, d);
+    hipError_t e = hipSetDevice(h->device);
+    if (e == hipSuccess) e = hipMemcpy(h->warena, host.data(), host.size(), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(&h->err, WENC_EHIP, "wenc_load: upload failed: %s", hipGetErrorString(e));
+    h->loaded = true;
+    return WENC_OK;
+}
+
+static int forward_impl(wenc_t *h, const float *mel, int32_t batch, float *out, void *stream, int tap, void *tap_dst) {
+    if (!h) return fail(nullptr, WENC_EINVAL, "wenc_forward: handle is NULL");
+    if (!h->loaded) return fail(&h->err, WENC_ESTATE, "wenc_forward: no weights loaded (call wenc_load first)");
+    if (batch < 0) return fail(&h->err, WENC_EINVAL, "wenc_forward: batch %d < 0", batch);
+    if (batch == 0) return WENC_OK;
+    if (!mel) return fail(&h->err, WENC_EINVAL, "wenc_forward: mel is NULL");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const wenc_config &c = h->cfg;
+    if (tap >= 0) {
+        if (!tap_dst) return fail(&h->err, WENC_EINVAL, "wenc_forward_tap: dst is NULL");
+        if (tap > WENC_TAP_BLOCK + c.n_layer - 1)
+            return fail(&h->err, WENC_EINVAL, "wenc_forward_tap: tap %d out of range", tap);
+        if (batch > c.max_batch)
+            return fail(&h->err, WENC_EINVAL, "wenc_forward_tap: batch %d > max_batch %d", batch, c.max_batch);
+        return h->forward_chunk(mel, batch, nullptr, st, tap, tap_dst);
+    }
+    if (!out) return fail(&h->err, WENC_EINVAL, "wenc_forward: out is NULL");
+    for (int b0 = 0; b0 < batch; b0 += c.max_batch) {
+        const int nb = batch - b0 < c.max_batch ? batch - b0 : c.max_batch;
+        WENC_TRY(h->forward_chunk(mel + size_t(b0) * c.n_frames * c.n_mels, nb, out + size_t(b0) * c.n_ctx * c.d_model, st,
+                                  -1, nullptr));
+    }
+    return WENC_OK;
+}
+
+int wenc_forward(wenc_t *h, const float *mel, int32_t batch, float *out, void *stream) {
+    return forward_impl(h, mel, batch, out, stream, -1, nullptr);
+}
+
+int wenc_forward_tap(wenc_t *h, const float *mel, int32_t batch, int32_t tap, void *dst, void *stream) {
+    if (h && tap < 0) return fail(&h->err, WENC_EINVAL, "wenc_forward_tap: tap %d < 0", tap);
+    return forward_impl(h, mel, batch, nullptr, stream, tap, dst);
+}
+
+void wenc_destroy(wenc_t *h) {
+    if (!h) return;
+    hipDeviceSynchronize();
+    for (auto &r : h->prof_pending) {
+        hipEventDestroy(r.e0);
+        hipEventDestroy(r.e1);
+    }
+    for (auto e : h->event_pool) hipEventDestroy(e);
+    if (h->warena) hipFree(h->warena);
+    if (h->sarena) hipFree(h->sarena);
+    delete h;
+}
+
+const char *wenc_last_error(const wenc_t *h) {
+    if (h) return h->err.c_str();
+    return g_err.c_str();
+}
+
+int wenc_k_layernorm(const float *x, const float *gamma, const float *beta, void *y, int32_t rows, int32_t d, float eps,
+                     int32_t out_f32, void *stream) {
+    if (const char *m = wk::layernorm_check(rows, d)) return fail(nullptr, WENC_EINVAL, "%s", m);
+    if (rows > 0 && (!x || !gamma || !beta || !y)) return fail(nullptr, WENC_EINVAL, "layernorm: null pointer");
+    const hipError_t e = wk::launch_layernorm(x, gamma, beta, y, rows, d, eps, out_f32 != 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? WENC_OK : fail(nullptr, WENC_EHIP, "layernorm: %s", hipGetErrorString(e));
+}
+
+int wenc_k_gemm(const wenc_gemm_args *args, void *stream) {
+    if (!args) return fail(nullptr, WENC_EINVAL, "gemm: args is NULL");
+    if (const char *m = wk::gemm_check(*args)) return fail(nullptr, WENC_EINVAL, "%s", m);
+    const hipError_t e = wk::launch_gemm(*args, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? WENC_OK : fail(nullptr, WENC_EHIP, "gemm: %s", hipGetErrorString(e));
+}
+
+int wenc_k_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, uint16_t *ao, int32_t batch,
+                     int32_t n_head, int32_t T, int32_t ldvt, void *stream) {
+    if (const char *m = wk::attention_check(batch, n_head, T, ldvt)) return fail(nullptr, WENC_EINVAL, "%s", m);
+    if (batch > 0 && (!q || !k || !vt || !ao)) return fail(nullptr, WENC_EINVAL, "attention: null pointer");
+    const hipError_t e = wk::launch_attention(q, k, vt, ao, batch, n_head, T, ldvt, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? WENC_OK : fail(nullptr, WENC_EHIP, "attention: %s", hipGetErrorString(e));
+}
+
+int wenc_profile(wenc_t *h, uint32_t site_mask) {
+    if (!h) return fail(nullptr, WENC_EINVAL, "wenc_profile: handle is NULL");
+    h->prof_mask = site_mask & ((1u << WENC_N_SITES) - 1);
+    return WENC_OK;
+}
+
+int wenc_profile_read(wenc_t *h, double *ms_total, int64_t *launches) {
+    if (!h) return fail(nullptr, WENC_EINVAL, "wenc_profile_read: handle is NULL");
+    if (!ms_total || !launches) return fail(&h->err, WENC_EINVAL, "wenc_profile_read: null output array");
+    for (int s = 0; s < WENC_N_SITES; ++s) {
+        ms_total[s] = 0.0;
+        launches[s] = 0;
+    }
+    int rc = WENC_OK;
+    for (auto &r : h->prof_pending) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(r.e1);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.e0, r.e1);
+        if (e != hipSuccess && rc == WENC_OK) rc = fail(&h->err, WENC_EHIP, "wenc_profile_read: %s", hipGetErrorString(e));
+        ms_total[r.site] += ms;
+        launches[r.site] += 1;
+        h->event_pool.push_back(r.e0);
+        h->event_pool.push_back(r.e1);
+    }
+    h->prof_pending.clear();
+    return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,242 @@
+"""ctypes binding of libwenc.so (C ABI in include/wenc.h).
+
+Argument marshalling only: every step of the encoder runs in the library's
+HIP kernels.  Device buffers are torch tensors (``.data_ptr()``) and the
+stream is torch's current HIP stream unless one is given.  The functions
+carry the C names; ``Encoder`` bundles create + load + forward.
+
+torch is imported before the library is loaded so that the library binds to
+the HIP runtime torch already loaded (both are ``libamdhip64.so.7``), which
+makes torch's stream handles and device pointers valid inside it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import torch
+
+from .configs import EncoderConfig
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwenc.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "wenc.h")
+
+WENC_OK, WENC_EINVAL, WENC_ENOMEM, WENC_ENODEV, WENC_ESTATE, WENC_EHIP = 0, -1, -2, -3, -4, -5
+WENC_TAP_C1, WENC_TAP_STEM, WENC_TAP_BLOCK = 0, 1, 2
+WENC_EPI_GELU_F16, WENC_EPI_CONV2, WENC_EPI_RESID, WENC_EPI_QKV = 0, 1, 2, 3
+SITES = ("ingest", "conv1", "conv2", "ln1", "qkv", "attn", "oproj", "ln2", "fc1", "fc2", "lnf")
+N_SITES = len(SITES)
+
+
+class WencError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"wenc error {code}: {msg}")
+        self.code = code
+
+
+class wenc_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("n_mels", "d_model", "n_head", "head_dim", "d_ff", "n_layer",
+                                              "n_frames", "n_ctx")] + \
+               [("ln_eps", ctypes.c_float), ("final_ln", ctypes.c_int32), ("max_batch", ctypes.c_int32)]
+
+
+class wenc_gemm_args(ctypes.Structure):
+    _fields_ = [
+        ("A", ctypes.c_void_p), ("a_batch_stride", ctypes.c_int64), ("a_rows_per_batch", ctypes.c_int32),
+        ("lda", ctypes.c_int32),
+        ("W", ctypes.c_void_p), ("ldw", ctypes.c_int32),
+        ("bias", ctypes.c_void_p),
+        ("C", ctypes.c_void_p), ("c_batch_stride", ctypes.c_int64), ("c_rows_per_batch", ctypes.c_int32),
+        ("c_row_offset", ctypes.c_int32), ("ldc", ctypes.c_int32),
+        ("pos", ctypes.c_void_p), ("pos_rows", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("vt", ctypes.c_void_p), ("T", ctypes.c_int32),
+        ("n_head", ctypes.c_int32), ("ldvt", ctypes.c_int32), ("q_scale", ctypes.c_float),
+        ("M", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("epilogue", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libwenc.so (once).  Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with `python -m whisper_audio_encoder_amd.build_lib`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(wenc_config)
+    L.wenc_create.argtypes = [cfgp, ctypes.POINTER(vp)]
+    L.wenc_create.restype = ctypes.c_int
+    L.wenc_weights_nbytes.argtypes = [cfgp]
+    L.wenc_weights_nbytes.restype = sz
+    L.wenc_load.argtypes = [vp, vp, sz]
+    L.wenc_load.restype = ctypes.c_int
+    L.wenc_forward.argtypes = [vp, vp, i32, vp, vp]
+    L.wenc_forward.restype = ctypes.c_int
+    L.wenc_forward_tap.argtypes = [vp, vp, i32, i32, vp, vp]
+    L.wenc_forward_tap.restype = ctypes.c_int
+    L.wenc_destroy.argtypes = [vp]
+    L.wenc_destroy.restype = None
+    L.wenc_last_error.argtypes = [vp]
+    L.wenc_last_error.restype = ctypes.c_char_p
+    L.wenc_k_layernorm.argtypes = [vp, vp, vp, vp, i32, i32, ctypes.c_float, i32, vp]
+    L.wenc_k_layernorm.restype = ctypes.c_int
+    L.wenc_k_gemm.argtypes = [ctypes.POINTER(wenc_gemm_args), vp]
+    L.wenc_k_gemm.restype = ctypes.c_int
+    L.wenc_k_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp]
+    L.wenc_k_attention.restype = ctypes.c_int
+    L.wenc_profile.argtypes = [vp, ctypes.c_uint32]
+    L.wenc_profile.restype = ctypes.c_int
+    L.wenc_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    L.wenc_profile_read.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/wenc.h declares."""
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wenc_[a-z_0-9]+)\s*\(", src)))
+
+
+def _check(rc: int, h=None):
+    if rc != WENC_OK:
+        raise WencError(rc, wenc_last_error(h))
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def make_config(cfg: EncoderConfig, max_batch: int | None = None) -> wenc_config:
+    return wenc_config(cfg.n_mels, cfg.d_model, cfg.n_head, cfg.head_dim, cfg.d_ff, cfg.n_layer,
+                       cfg.n_frames, cfg.n_ctx, cfg.ln_eps, cfg.final_ln,
+                       cfg.batch if max_batch is None else max_batch)
+
+
+# ---------------------------------------------------------------- C names
+def wenc_last_error(h=None) -> str:
+    return lib().wenc_last_error(h).decode()
+
+
+def wenc_weights_nbytes(cfg: wenc_config) -> int:
+    return lib().wenc_weights_nbytes(ctypes.byref(cfg))
+
+
+def wenc_create(cfg: wenc_config) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(lib().wenc_create(ctypes.byref(cfg), ctypes.byref(h)))
+    return h
+
+
+def wenc_load(h, blob: np.ndarray) -> None:
+    blob = np.ascontiguousarray(blob).view(np.uint8)
+    _check(lib().wenc_load(h, blob.ctypes.data, blob.nbytes), h)
+
+
+def wenc_forward(h, mel: torch.Tensor, batch: int, out: torch.Tensor, stream=None) -> None:
+    _check(lib().wenc_forward(h, _ptr(mel), batch, _ptr(out), _stream(stream)), h)
+
+
+def wenc_forward_tap(h, mel: torch.Tensor, batch: int, tap: int, dst: torch.Tensor, stream=None) -> None:
+    _check(lib().wenc_forward_tap(h, _ptr(mel), batch, tap, _ptr(dst), _stream(stream)), h)
+
+
+def wenc_destroy(h) -> None:
+    lib().wenc_destroy(h)
+
+
+def wenc_k_layernorm(x, gamma, beta, y, rows, d, eps, out_f32, stream=None) -> None:
+    _check(lib().wenc_k_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, d, eps, int(out_f32),
+                                  _stream(stream)))
+
+
+def wenc_k_gemm(args: wenc_gemm_args, stream=None) -> None:
+    _check(lib().wenc_k_gemm(ctypes.byref(args), _stream(stream)))
+
+
+def wenc_k_attention(q, k, vt, ao, batch, n_head, T, ldvt, stream=None) -> None:
+    _check(lib().wenc_k_attention(_ptr(q), _ptr(k), _ptr(vt), _ptr(ao), batch, n_head, T, ldvt, _stream(stream)))
+
+
+def wenc_profile(h, site_mask: int) -> None:
+    _check(lib().wenc_profile(h, site_mask), h)
+
+
+def wenc_profile_read(h) -> dict:
+    ms = (ctypes.c_double * N_SITES)()
+    n = (ctypes.c_int64 * N_SITES)()
+    _check(lib().wenc_profile_read(h, ms, n), h)
+    return {SITES[i]: (ms[i], n[i]) for i in range(N_SITES)}
+
+
+# ---------------------------------------------------------------- wrapper
+class Encoder:
+    """One loaded encoder on the current device."""
+
+    def __init__(self, cfg: EncoderConfig, blob: np.ndarray, max_batch: int | None = None):
+        self.cfg = cfg
+        self.ccfg = make_config(cfg, max_batch)
+        self.h = wenc_create(self.ccfg)
+        try:
+            wenc_load(self.h, blob)
+        except Exception:
+            wenc_destroy(self.h)
+            self.h = None
+            raise
+
+    def _check_mel(self, mel: torch.Tensor):
+        c = self.cfg
+        if not (mel.is_cuda and mel.dtype == torch.float32 and mel.is_contiguous()):
+            raise ValueError("mel must be a contiguous fp32 device tensor")
+        if mel.dim() != 3 or mel.shape[1:] != (c.n_frames, c.n_mels):
+            raise ValueError(f"mel must be [batch, {c.n_frames}, {c.n_mels}], got {tuple(mel.shape)}")
+
+    def forward(self, mel: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        self._check_mel(mel)
+        c = self.cfg
+        B = mel.shape[0]
+        if out is None:
+            out = torch.empty((B, c.n_ctx, c.d_model), dtype=torch.float32, device=mel.device)
+        elif not (out.is_cuda and out.dtype == torch.float32 and out.is_contiguous()
+                  and tuple(out.shape) == (B, c.n_ctx, c.d_model)):
+            raise ValueError("out must be a contiguous fp32 device tensor [batch, n_ctx, d_model]")
+        wenc_forward(self.h, mel, B, out, stream)
+        return out
+
+    def tap(self, mel: torch.Tensor, tap: int, stream=None) -> torch.Tensor:
+        self._check_mel(mel)
+        c = self.cfg
+        B = mel.shape[0]
+        if tap == WENC_TAP_C1:
+            dst = torch.empty((B, c.n_frames, c.d_model), dtype=torch.float16, device=mel.device)
+        else:
+            dst = torch.empty((B, c.n_ctx, c.d_model), dtype=torch.float32, device=mel.device)
+        wenc_forward_tap(self.h, mel, B, tap, dst, stream)
+        return dst
+
+    def close(self):
+        if self.h is not None:
+            wenc_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
