@@ -323,9 +323,6 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s) {
     p.M = a.M;
     p.N = a.N;
     p.K = a.K;
-    // Large tiles when they still give at least two workgroups per CU.
-    const long big_tiles = long((a.M + 255) / 256) * ((a.N + 255) / 256);
-    if (big_tiles >= 512) return launch_cfg<256, 256, 128, 128>(p, a.epilogue, s);
     return launch_cfg<128, 128, 64, 64>(p, a.epilogue, s);
 }
 
