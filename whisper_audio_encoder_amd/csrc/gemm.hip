@@ -10,15 +10,23 @@
 // (kernels.nu, wk_matvec: W[rows][cols]), so W rows are K-contiguous, which
 // is exactly the operand layout v_mfma_f32_32x32x16_f16 reads per lane.
 //
-// Structure: a 256-thread workgroup (4 wave64s) owns a BM x BN output tile
-// and walks K in steps of 64.  Each step is staged through LDS with 16-byte
-// chunks XOR-swizzled by row (chunk c of row r lives at c ^ (r & 7)) so the
-// 16-byte fragment reads of 8 consecutive rows hit distinct banks.  LDS is
-// double buffered: the next K step's global loads are in flight while the
-// current step's MFMAs run, and one barrier per step separates them.
-// Workgroup ids are remapped so each XCD (ids are dealt round-robin over the
-// 8 XCDs) receives a contiguous run of tiles, ordered in groups of 8 tile
-// rows, so tiles sharing A rows or W rows share that XCD's L2.
+// Structure (details at each step below).  A workgroup of NW wave64s owns a BM x BN output tile and walks
+// K in steps of 64.  Each step is moved from global memory straight into LDS
+// by buffer_load ... lds (no VGPR staging); a buffer offset with bit 31 set
+// lies beyond the descriptor's range and reads as zero, which pads the M, N
+// and K tails without branches.  Within LDS, 16-byte chunks are XOR-swizzled
+// by row so that fragment reads are free of bank conflicts; the direct loads
+// produce that layout by choosing which global chunk each lane fetches.  LDS is double
+// buffered: step k+1 is in flight while step k's MFMAs run, with one barrier
+// per step.  The MFMA takes W as its A operand and A^T as its B operand, so
+// each lane ends up owning one output row and runs of 4 consecutive output
+// columns, which the epilogues store as 8- or 16-byte vectors.
+//
+// Workgroup ids are remapped so that each XCD (ids are dealt round-robin
+// over the 8 XCDs) receives a contiguous run of tiles, ordered in groups of
+// 8 tile rows, so tiles sharing A rows or W rows share that XCD's L2.
+#include <cstdlib>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -27,6 +35,7 @@ namespace wk {
 namespace {
 
 constexpr int BK = 64;
+constexpr uint32_t OOB = 0x80000000u;  // buffer offset beyond num_records: reads 0
 
 struct GemmP {
     const f16 *A;
@@ -65,85 +74,152 @@ __device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int t
     tn = in / gm;
 }
 
+// Element offset of A row m (batch remap for the conv stem's frame windows).
+__device__ __forceinline__ int64_t a_row(const GemmP &p, uint32_t m) {
+    const uint32_t bi = divu(m, p.a_div);
+    return int64_t(bi) * p.a_bs + int64_t(m - bi * p.a_div.d) * p.lda;
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor over [base, base + 2 GiB): raw (stride 0), so an offset
+// at or past num_records reads as zero.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
+    r[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffff));
+    r[2] = 0x7fffffff;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// One 16-byte-per-lane global -> LDS transfer of 1 KB: lane i's data lands
+// at lds + 16 i.  Written as inline assembly so that the compiler does not
+// see an LDS store: it would otherwise wait for every such transfer before
+// later LDS reads of the other buffer.  The main loop orders the transfers
+// itself (s_waitcnt vmcnt(0) + barrier before any wave reads the buffer
+// they fill).  M0 carries the LDS address; nothing else in these kernels
+// uses M0.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, const f16 *lds, uint32_t voffset) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) f16 *)lds)));
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(m0), "v"(voffset), "s"(rsrc)
+        : "memory");
+}
+
+// LDS chunk swizzle.  A tile row is 128 B (8 chunks of 16 B); logical chunk c
+// of row r is stored at chunk position c ^ swz(r).  The LDS serves a 16-byte
+// read for 16 lanes per cycle across 64 banks, i.e. two 128-byte rows'
+// worth: the 16 rows read together must cover the 16 (row parity, chunk
+// position) pairs, which this XOR on bits 1..3 of the row guarantees.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
+// Store 4 consecutive output columns n .. n+3 of row m.
 template <int EPI>
-__device__ __forceinline__ void epi_store(const GemmP &p, int m, int n, float v) {
+__device__ __forceinline__ void epi_store4(const GemmP &p, int m, int n, f32x4 v) {
+    const f32x4 b = ld4(p.bias + n);
     if constexpr (EPI == WENC_EPI_GELU_F16) {
         const uint32_t bi = divu(m, p.c_div);
         const uint32_t r = m - bi * p.c_div.d;
-        f16 *C = static_cast<f16 *>(p.C) + bi * p.c_bs + int64_t(r + p.c_off) * p.ldc + n;
-        *C = (f16)gelu_erf(v + p.bias[n]);
+        f16 *C = static_cast<f16 *>(p.C) + int64_t(bi) * p.c_bs + int64_t(r + p.c_off) * p.ldc + n;
+        f16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (f16)gelu_erf(v[e] + b[e]);
+        *reinterpret_cast<f16x4 *>(C) = o;
     } else if constexpr (EPI == WENC_EPI_CONV2) {
         const uint32_t t = m - divu(m, p.pos_div) * p.pos_div.d;
-        float *C = static_cast<float *>(p.C) + int64_t(m) * p.ldc + n;
-        *C = gelu_erf(v + p.bias[n]) + p.pos[int64_t(t) * p.N + n];
+        const f32x4 ps = ld4(p.pos + int64_t(t) * p.N + n);
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = gelu_erf(v[e] + b[e]) + ps[e];
+        *reinterpret_cast<f32x4 *>(static_cast<float *>(p.C) + int64_t(m) * p.ldc + n) = o;
     } else if constexpr (EPI == WENC_EPI_RESID) {
-        float *C = static_cast<float *>(p.C) + int64_t(m) * p.ldc + n;
-        *C += v + p.bias[n];
+        f32x4 *C = reinterpret_cast<f32x4 *>(static_cast<float *>(p.C) + int64_t(m) * p.ldc + n);
+        *C = *C + v + b;
+    } else if constexpr (EPI == WENC_EPI_QKV) {
+        const int slice = n / p.dmodel;
+        const int c = n - slice * p.dmodel;
+        const int h = c >> 6, e = c & 63;
+        const uint32_t bb = divu(m, p.t_div);
+        const uint32_t t = m - bb * p.t_div.d;
+        const int64_t bh = int64_t(bb) * p.H + h;
+        if (slice < 2) {
+            const float sc = slice == 0 ? p.q_scale : 1.0f;
+            f16x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = (f16)((v[i] + b[i]) * sc);
+            f16 *dst = slice == 0 ? p.q : p.k;
+            *reinterpret_cast<f16x4 *>(dst + (bh * p.t_div.d + t) * 64 + e) = o;
+        } else {
+            f16 *dst = p.vt + (bh * 64 + e) * p.ldvt + t;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[int64_t(i) * p.ldvt] = (f16)(v[i] + b[i]);
+        }
     }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
-__global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(1, 2)))
+template <int BM, int BN, int WM, int WN, int NW, int EPI>
+__global__ void __launch_bounds__(NW * 64)
 gemm_kernel(const GemmP p) {
     constexpr int WAVES_N = BN / WN;
-    static_assert((BM / WM) * (BN / WN) == 4, "4 waves per workgroup");
+    static_assert((BM / WM) * (BN / WN) == NW, "wave grid");
     constexpr int TM = WM / 32, TN = WN / 32;
-    constexpr int AL = BM * (BK / 8) / 256;
-    constexpr int BL = BN * (BK / 8) / 256;
-    __shared__ __attribute__((aligned(16))) f16 smem[2 * (BM + BN) * BK];
-    f16 *As = smem;
-    f16 *Bs = smem + 2 * BM * BK;
+    constexpr int AG = BM / 8 / NW;  // 8-row groups of A each wave moves per step
+    constexpr int BG = BN / 8 / NW;
+    static_assert(AG >= 1 && BG >= 1, "each wave moves at least one group");
+    constexpr int STAGE = (BM + BN) * BK;  // halves per LDS stage
+    __shared__ __attribute__((aligned(1024))) f16 smem0[STAGE];
+    __shared__ __attribute__((aligned(1024))) f16 smem1[STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS addresses stay scalar
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     int tm, tn;
     tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    // Global -> LDS staging: thread t moves 16-byte chunk (t & 7) of rows
-    // (t >> 3) + 32 i.  The chunk's k offset is the same for every i.
-    const int ck = tid & 7;
-    const f16 *a_src[AL];
-    bool a_ok[AL];
-    int a_dst[AL];
+    // Direct loads: one instruction moves 8 tile rows x 128 B; lane i lands at
+    // row r = 8 g + (i >> 3), chunk position i & 7, so it fetches logical
+    // chunk (i & 7) ^ sw(r).
+    const int64_t a0 = a_row(p, m0);
+    uint32_t a_off[AG], a_ch[AG];
 #pragma unroll
-    for (int i = 0; i < AL; ++i) {
-        const int r = (tid >> 3) + 32 * i;
+    for (int g = 0; g < AG; ++g) {
+        const int r = (wave * AG + g) * 8 + (lane >> 3);
+        a_ch[g] = (lane & 7) ^ swz(r);
         const int m = m0 + r;
-        a_ok[i] = m < p.M;
-        const uint32_t mm = a_ok[i] ? m : 0;
-        const uint32_t bi = divu(mm, p.a_div);
-        a_src[i] = p.A + bi * p.a_bs + int64_t(mm - bi * p.a_div.d) * p.lda + ck * 8;
-        a_dst[i] = r * BK + ((ck ^ (r & 7)) << 3);
+        a_off[g] = m < p.M ? uint32_t((a_row(p, m) - a0) * 2) + a_ch[g] * 16 : OOB;
     }
-    const f16 *b_src[BL];
-    bool b_ok[BL];
-    int b_dst[BL];
+    uint32_t b_off[BG], b_ch[BG];
 #pragma unroll
-    for (int i = 0; i < BL; ++i) {
-        const int r = (tid >> 3) + 32 * i;
-        const int n = n0 + r;
-        b_ok[i] = n < p.N;
-        b_src[i] = p.W + int64_t(b_ok[i] ? n : 0) * p.ldw + ck * 8;
-        b_dst[i] = r * BK + ((ck ^ (r & 7)) << 3);
+    for (int g = 0; g < BG; ++g) {
+        const int r = (wave * BG + g) * 8 + (lane >> 3);
+        b_ch[g] = (lane & 7) ^ swz(r);
+        b_off[g] = n0 + r < p.N ? uint32_t(r * p.ldw * 2 + b_ch[g] * 16) : OOB;
     }
+    const i32x4 ra = make_rsrc(p.A + a0);
+    const i32x4 rb = make_rsrc(p.W + int64_t(n0) * p.ldw);
 
-    uint4 ra[AL], rb[BL];
-    auto gload = [&](int kt) {
-        const bool kok = kt * BK + ck * 8 < p.K;
+    auto issue = [&](int kt, f16 *st) {
+        const uint32_t kb = uint32_t(kt) * (BK * 2);
 #pragma unroll
-        for (int i = 0; i < AL; ++i)
-            ra[i] = (a_ok[i] && kok) ? *reinterpret_cast<const uint4 *>(a_src[i] + kt * BK) : make_uint4(0, 0, 0, 0);
+        for (int g = 0; g < AG; ++g) {
+            const uint32_t kflag = (kt * BK + int(a_ch[g]) * 8 < p.K) ? 0u : OOB;
+            load_lds16(ra, st + (wave * AG + g) * 8 * BK, (a_off[g] | kflag) + kb);
+        }
 #pragma unroll
-        for (int i = 0; i < BL; ++i)
-            rb[i] = (b_ok[i] && kok) ? *reinterpret_cast<const uint4 *>(b_src[i] + kt * BK) : make_uint4(0, 0, 0, 0);
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < AL; ++i) *reinterpret_cast<uint4 *>(As + buf * BM * BK + a_dst[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < BL; ++i) *reinterpret_cast<uint4 *>(Bs + buf * BN * BK + b_dst[i]) = rb[i];
+        for (int g = 0; g < BG; ++g) {
+            const uint32_t kflag = (kt * BK + int(b_ch[g]) * 8 < p.K) ? 0u : OOB;
+            load_lds16(rb, st + BM * BK + (wave * BG + g) * 8 * BK, (b_off[g] | kflag) + kb);
+        }
     };
 
     f32x16 acc[TM][TN];
@@ -154,109 +230,128 @@ gemm_kernel(const GemmP p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int nk = (p.K + BK - 1) / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-
-    // Fragment reads: lane l supplies row (l & 31) of a 32-row tile and the
-    // 8 k values 8 (l >> 5) .. +7 of the current 16-wide k slice.
+    // Fragment reads: lane supplies row (lane & 31) of a 32-row tile and k
+    // values 8 (lane >> 5) .. +7 of the current 16-wide slice.  Two fragment
+    // sets alternate so the reads of slice kk+1 are in flight during the
+    // MFMAs of slice kk; sched_barrier keeps the compiler from hoisting every
+    // read of the step up front (which would need 4 sets of registers).
     const int frow = lane & 31;
-    const int fsw = lane & 7;  // == row & 7 for every fragment row of this lane
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-        const f16 *as = As + cur * BM * BK + (wm * WM + frow) * BK;
-        const f16 *bs = Bs + cur * BN * BK + (wn * WN + frow) * BK;
+    const int fsw = swz(lane & 31);  // == swz(row) for every fragment row of this lane
+    auto load_frags = [&](const f16 *st, int kk, f16x8 (&af)[TM], f16x8 (&bf)[TN]) {
+        const f16 *as = st + (wm * WM + frow) * BK;
+        const f16 *bs = st + BM * BK + (wn * WN + frow) * BK;
+        const int ch = ((kk * 2 + (lane >> 5)) ^ fsw) << 3;
+        // read in the order the MFMAs below consume them: b0, a0 .. a(TM-1), b1 ..
+        bf[0] = *reinterpret_cast<const f16x8 *>(bs + ch);
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int ch = ((kk * 2 + (lane >> 5)) ^ fsw) << 3;
-            f16x8 af[TM], bf[TN];
+        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const f16x8 *>(as + i * 32 * BK + ch);
 #pragma unroll
-            for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const f16x8 *>(as + i * 32 * BK + ch);
+        for (int j = 1; j < TN; ++j) bf[j] = *reinterpret_cast<const f16x8 *>(bs + j * 32 * BK + ch);
+    };
+    auto mfmas = [&](const f16x8 (&af)[TM], const f16x8 (&bf)[TN]) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const f16x8 *>(bs + j * 32 * BK + ch);
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int i = 0; i < TM; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    };
+    // Interleave the next slice's fragment reads with this slice's MFMAs:
+    // one LDS read, then MFMAs, repeated, so every read has several MFMAs
+    // (32 cycles each) to land before its consumer.
+    auto interleave = [&]() {
+        constexpr int NR = TM + TN, NM = TM * TN;
+        constexpr int PER = NM / NR > 0 ? NM / NR : 1;
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int r = 0; r < NR; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMA
         }
-        if (kt + 1 < nk) sstore(cur ^ 1);
-        __syncthreads();
+        if constexpr (NM > NR * PER) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR * PER, 0);
+    };
+    static_assert(BK == 64, "the main loop walks four 16-wide k slices per step");
+
+    // Main loop.  Slice kk of step kt is read into fragment set (kk & 1)
+    // while the MFMAs of slice kk-1 run.  The barrier that publishes step
+    // kt+1 sits before the MFMAs of the last slice of step kt (whose
+    // fragments are already in registers), so those MFMAs overlap both the
+    // barrier and the first fragment reads of step kt+1, and the direct
+    // loads of step kt+2 go into the buffer step kt has just released.
+    // Steps alternate between the two LDS buffers in a loop unrolled by
+    // two, so every LDS access names its buffer statically and the compiler
+    // can tell a transfer into one buffer from reads of the other.
+    const int nk = (p.K + BK - 1) / BK;
+    f16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    auto step = [&](int kt, f16 *cur, f16 *nxt) {
+        load_frags(cur, 1, fa1, fb1);
+        mfmas(fa0, fb0);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(cur, 2, fa0, fb0);
+        mfmas(fa1, fb1);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(cur, 3, fa1, fb1);
+        mfmas(fa0, fb0);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < nk) {
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (kt + 2 < nk) issue(kt + 2, cur);
+            load_frags(nxt, 0, fa0, fb0);
+        }
+        mfmas(fa1, fb1);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    issue(0, smem0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (nk > 1) issue(1, smem1);
+    load_frags(smem0, 0, fa0, fb0);
+#pragma unroll 1
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, smem0, smem1);
+        if (kt + 1 < nk) step(kt + 1, smem1, smem0);
     }
 
-    // Epilogue.  Accumulator register r of a 32x32 tile holds row
-    // 8 (r >> 2) + 4 (lane >> 5) + (r & 3) and column lane & 31.
+    // Epilogue: register r of tile (i, j) holds row m = (lane & 31) of the
+    // i-th 32-row block and column 8 (r >> 2) + 4 (lane >> 5) + (r & 3).
     const int hh = lane >> 5;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + j * 32 + (lane & 31);
-        if (n >= p.N) continue;
-        if constexpr (EPI == WENC_EPI_QKV) {
-            const int slice = n / p.dmodel;
-            const int c = n - slice * p.dmodel;
-            const int h = c >> 6, e = c & 63;
-            const float bn = p.bias[n];
+    for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wm * WM + i * 32 + frow;
+        if (m >= p.M) continue;
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int mb = m0 + wm * WM + i * 32 + 8 * g + 4 * hh;
-                    if (slice < 2) {
-                        f16 *dst = slice == 0 ? p.q : p.k;
-                        const float sc = slice == 0 ? p.q_scale : 1.0f;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int m = mb + r;
-                            if (m < p.M) {
-                                const uint32_t b = divu(m, p.t_div);
-                                const uint32_t t = m - b * p.t_div.d;
-                                dst[((int64_t(b) * p.H + h) * p.t_div.d + t) * 64 + e] =
-                                    (f16)((acc[i][j][4 * g + r] + bn) * sc);
-                            }
-                        }
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int m = mb + r;
-                            if (m < p.M) {
-                                const uint32_t b = divu(m, p.t_div);
-                                const uint32_t t = m - b * p.t_div.d;
-                                p.vt[((int64_t(b) * p.H + h) * 64 + e) * p.ldvt + t] =
-                                    (f16)(acc[i][j][4 * g + r] + bn);
-                            }
-                        }
-                    }
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * hh;
+                if (n < p.N) {
+                    f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    epi_store4<EPI>(p, m, n, v);
                 }
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (m < p.M) epi_store<EPI>(p, m, n, acc[i][j][r]);
-                }
-        }
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NW>
 hipError_t launch_cfg(const GemmP &base, int epi, hipStream_t s) {
     GemmP p = base;
     p.tiles_m = (p.M + BM - 1) / BM;
     p.tiles_n = (p.N + BN - 1) / BN;
-    const dim3 grid(p.tiles_m * p.tiles_n), block(256);
+    const dim3 grid(p.tiles_m * p.tiles_n), block(NW * 64);
     switch (epi) {
-        case WENC_EPI_GELU_F16: gemm_kernel<BM, BN, WM, WN, WENC_EPI_GELU_F16><<<grid, block, 0, s>>>(p); break;
-        case WENC_EPI_CONV2: gemm_kernel<BM, BN, WM, WN, WENC_EPI_CONV2><<<grid, block, 0, s>>>(p); break;
-        case WENC_EPI_RESID: gemm_kernel<BM, BN, WM, WN, WENC_EPI_RESID><<<grid, block, 0, s>>>(p); break;
-        case WENC_EPI_QKV: gemm_kernel<BM, BN, WM, WN, WENC_EPI_QKV><<<grid, block, 0, s>>>(p); break;
+        case WENC_EPI_GELU_F16: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_GELU_F16><<<grid, block, 0, s>>>(p); break;
+        case WENC_EPI_CONV2: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_CONV2><<<grid, block, 0, s>>>(p); break;
+        case WENC_EPI_RESID: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_RESID><<<grid, block, 0, s>>>(p); break;
+        case WENC_EPI_QKV: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_QKV><<<grid, block, 0, s>>>(p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
+
+int g_tile_override = -1;  // WENC_GEMM_TILE: 0 = 128x128, 1 = 256x256 x 8 waves, 2 = 256x256 x 4 waves
 
 }  // namespace
 
@@ -265,9 +360,16 @@ const char *gemm_check(const wenc_gemm_args &a) {
     if (a.M < 0 || a.N <= 0 || a.K <= 0) return "gemm: need M >= 0, N > 0, K > 0";
     if (a.K % 8 || a.lda % 8 || a.ldw % 8 || a.a_batch_stride % 8)
         return "gemm: K, lda, ldw and a_batch_stride must be multiples of 8 (16-byte rows)";
+    if (a.N % 4 || a.ldc % 4 || a.c_batch_stride % 4)
+        return "gemm: N, ldc and c_batch_stride must be multiples of 4 (vector stores)";
     if (a.ldw < a.K) return "gemm: ldw < K";
     if (a.a_rows_per_batch <= 0 || a.a_rows_per_batch >= (1 << 16)) return "gemm: a_rows_per_batch out of [1, 65535]";
     if (a.M >= (1 << 24)) return "gemm: M must be < 2^24";
+    // per-tile buffer offsets are 31-bit: a 256-row tile of A (which may
+    // straddle two batch items) and of W must span well under 2 GiB
+    if (int64_t(a.lda) * 256 * 2 + int64_t(a.a_batch_stride) * 2 >= (int64_t(1) << 30) ||
+        int64_t(a.ldw) * 256 * 2 >= (int64_t(1) << 30))
+        return "gemm: operand rows too long for 31-bit tile offsets";
     switch (a.epilogue) {
         case WENC_EPI_GELU_F16:
             if (!a.C) return "gemm: C is null";
@@ -323,7 +425,21 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s) {
     p.M = a.M;
     p.N = a.N;
     p.K = a.K;
-    return launch_cfg<128, 128, 64, 64>(p, a.epilogue, s);
+    if (g_tile_override < 0) {
+        const char *e = std::getenv("WENC_GEMM_TILE");
+        g_tile_override = e ? std::atoi(e) : 99;
+    }
+    int cfg = g_tile_override;
+    if (cfg > 2) {
+        // 256 x 256 tiles when they fill the 256 CUs nearly twice over
+        const long big = long((a.M + 255) / 256) * ((a.N + 255) / 256);
+        cfg = big >= 448 ? 1 : 0;
+    }
+    switch (cfg) {
+        case 1: return launch_cfg<256, 256, 128, 64, 8>(p, a.epilogue, s);
+        case 2: return launch_cfg<256, 256, 128, 128, 4>(p, a.epilogue, s);
+        default: return launch_cfg<128, 128, 64, 64, 4>(p, a.epilogue, s);
+    }
 }
 
 }  // namespace wk
