@@ -150,9 +150,12 @@ enum {
  *     + (m % c_rows_per_batch + c_row_offset) * ldc.
  * QKV: N = 3 * n_head * 64; columns [0, d) go to q and [d, 2d) to k as
  * [batch][n_head][T][64] fp16, columns [2d, 3d) to vt as
- * [batch][n_head][64][ldvt] fp16 (keys contiguous), with m = b * T + t;
- * the q slice is multiplied by q_scale after its bias.  Requires K % 8 == 0,
- * lda % 8 == 0, ldw % 8 == 0, a_batch_stride % 8 == 0, M * ... < 2^24. */
+ * [batch][n_head][64][ldvt] fp16 with m = b * T + t, where key t of a row
+ * sits at slot t with bits 2 and 3 swapped (the order the attention kernel
+ * consumes) and the slots of keys T .. ldvt-1 are written with zeros; the q
+ * slice is multiplied by q_scale after its bias.  Requires K % 8 == 0,
+ * lda % 8 == 0, ldw % 8 == 0, a_batch_stride % 8 == 0, N, ldc and
+ * c_batch_stride multiples of 4, ldvt a multiple of 64, M < 2^24. */
 typedef struct wenc_gemm_args {
     const uint16_t *A; int64_t a_batch_stride; int32_t a_rows_per_batch; int32_t lda;
     const uint16_t *W; int32_t ldw;
@@ -166,10 +169,13 @@ typedef struct wenc_gemm_args {
 int wenc_k_gemm(const wenc_gemm_args *args, void *stream);
 
 /* Non-causal attention per (batch, head) (kernels.nu, wk_attn with causal 0):
- *   ao[b][t][h*64 + e] = sum_u softmax_u(q[b][h][t] . k[b][h][u]) * vt[b][h][e][u]
+ *   ao[b][t][h*64 + e] = sum_u softmax_u(q[b][h][t] . k[b][h][u]) * v[b][h][u][e]
  * with q ALREADY scaled by log2(e)/sqrt(64) (the softmax is taken in base 2),
- * q, k fp16 [batch][n_head][T][64], vt fp16 [batch][n_head][64][ldvt],
- * ao fp16 [batch][T][n_head*64].  ldvt % 8 == 0, ldvt >= T. */
+ * q, k fp16 [batch][n_head][T][64], ao fp16 [batch][T][n_head*64], and v
+ * given transposed as vt fp16 [batch][n_head][64][ldvt] in the key-slot
+ * order the QKV epilogue writes (key u at slot u with bits 2 and 3 swapped);
+ * slots of keys T .. ldvt-1 must hold finite values.  ldvt % 64 == 0,
+ * ldvt >= T. */
 int wenc_k_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, uint16_t *ao,
                      int32_t batch, int32_t n_head, int32_t T, int32_t ldvt, void *stream);
 

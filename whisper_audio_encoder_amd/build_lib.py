@@ -23,6 +23,10 @@ LIB = os.path.join(PKG, "libwenc.so")
 
 SOURCES = ["gemm.hip", "attention.hip", "layernorm.hip", "wenc_runtime.cpp"]
 
+# Per-source flags.  Attention runs softmax VALU work on the MFMA results:
+# keeping them in ordinary VGPRs avoids copies between AGPRs and VGPRs.
+EXTRA_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -42,7 +46,7 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so; drop that line only
     noise = "'-packed-fp32-ops' is not a recognized feature"

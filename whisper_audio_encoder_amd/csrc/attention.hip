@@ -8,18 +8,21 @@
 // stream amortised over many queries); the layout below is our own.
 //
 // One 256-thread workgroup takes 128 queries of one (b, h); each wave64 owns
-// 32 of them.  Key tiles of 64 keys stream through LDS (double buffered):
-// K as [key][64] and V^T as [dim][key], both in 16-byte chunks XOR-swizzled
-// by row.  Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_f16, so a
-// lane holds 32 scores of ONE query: the row max and row sum are in-lane
-// reductions plus one exchange with lane ^ 32.  The probabilities are then
-// already laid out as the B operand of O^T += V^T P^T; the order in which a
-// lane holds its keys (4 consecutive keys, skip 4) is matched by storing
-// each 16-key group of V^T in LDS in that same order.
+// 32 of them and keeps them in registers.  Key tiles of 64 keys stream into
+// LDS by direct buffer loads (double buffered), K as [key][64] and V^T as
+// [dim][key slot], 16-byte chunks XOR-swizzled by row.  Each wave computes
+// S^T = K Q^T with v_mfma_f32_32x32x16_f16, so a lane holds 32 scores of ONE
+// query: the row max and row sum are in-lane reductions plus one exchange
+// with lane ^ 32.  The probabilities are then laid out as the B operand of
+// O^T += V^T P^T, except that a lane holds its keys in runs of 4 (4 keys,
+// skip 4).  The producer of V^T stores each 16-key group in exactly that
+// order (key slot = key with bits 2 and 3 swapped), so one 16-byte LDS read
+// gives a lane the 8 values of V^T it multiplies.
 //
 // q arrives multiplied by log2(e) / 8, so the softmax is evaluated with
-// exp2 and no further scaling.  Keys at or beyond T (the last tile of a
-// 1500-key window) get score -inf and zero V.
+// exp2 and no further scaling.  Keys at or beyond T get score -inf; their
+// K rows read as zero (outside the buffer range) and their V^T slots must
+// hold finite values (the producer writes zeros there).
 #include "common.h"
 #include "kernels.h"
 
@@ -30,19 +33,53 @@ namespace {
 constexpr int QT = 128;  // queries per workgroup
 constexpr int KT = 64;   // keys per tile
 
+// LDS chunk swizzle of a 128-byte row: conflict-free 16-byte reads for the 16
+// lanes the LDS serves per cycle across its 64 banks.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t nbytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
+    r[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffff));
+    r[2] = __builtin_amdgcn_readfirstlane(int(nbytes));
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 1 KB global -> LDS transfer (lane i's 16 bytes land at lds + 16 i); an
+// offset past the descriptor's range reads zero.  Inline assembly so the
+// compiler does not serialise later LDS reads of the other buffer behind it;
+// the loop orders it with s_waitcnt vmcnt(0) + barrier.  M0 carries the LDS
+// address and is used by nothing else in this kernel.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, const f16 *lds, uint32_t voffset) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) f16 *)lds)));
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(m0), "v"(voffset), "s"(rsrc)
+        : "memory");
+}
+
 __global__ void __launch_bounds__(256)
 attn_kernel(const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__restrict__ vt,
             f16 *__restrict__ ao, int T, int H, int ldvt) {
     const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, l32 = lane & 31;
     const int64_t bh = int64_t(b) * H + h;
     const f16 *Q = q + bh * T * 64;
-    const f16 *K = k + bh * T * 64;
-    const f16 *VT = vt + bh * 64 * ldvt;
 
-    __shared__ __attribute__((aligned(16))) f16 Ks[2][KT * 64];
-    __shared__ __attribute__((aligned(16))) f16 Vs[2][64 * KT];
+    __shared__ __attribute__((aligned(1024))) f16 Ks0[KT * 64];
+    __shared__ __attribute__((aligned(1024))) f16 Vs0[64 * KT];
+    __shared__ __attribute__((aligned(1024))) f16 Ks1[KT * 64];
+    __shared__ __attribute__((aligned(1024))) f16 Vs1[64 * KT];
 
     // Q^T fragments (B operand): lane supplies query l32, dims 16 kk + 8 hh .. +7.
     const int qrow = qt * QT + wave * 32 + l32;
@@ -55,41 +92,25 @@ attn_kernel(const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__r
             qf[kk] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
 
-    // Tile staging: thread moves 16-byte chunk (tid & 7) of rows (tid >> 3) and (tid >> 3) + 32.
-    const int ck = tid & 7;
-    uint4 rk[2], rv[2];
-    auto gload = [&](int kt) {
+    // Tile transfers: each wave moves rows 16 wave .. 16 wave + 15 of the K
+    // tile and of the V^T tile (two 8-row groups each).  Lane i lands at row
+    // 8 g + (i >> 3), chunk position i & 7, so it fetches logical chunk
+    // (i & 7) ^ swz(row).
+    const i32x4 rk = make_rsrc(k + bh * T * 64, uint32_t(T) * 128u);
+    const i32x4 rv = make_rsrc(vt + bh * 64 * ldvt, uint32_t(ldvt) * 128u);
+    uint32_t k_off[2], v_off[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = (tid >> 3) + 32 * i;
-            const int key = kt * KT + r;
-            rk[i] = key < T ? *reinterpret_cast<const uint4 *>(K + int64_t(key) * 64 + ck * 8) : make_uint4(0, 0, 0, 0);
-            const int k0 = kt * KT + ck * 8;  // first key of this V^T chunk (row r = dim)
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (k0 < T) {
-                v = *reinterpret_cast<const uint4 *>(VT + int64_t(r) * ldvt + k0);
-                if (k0 + 8 > T) {
-                    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int g = 0; g < 2; ++g) {
+        const int r = (wave * 2 + g) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
+        k_off[g] = uint32_t(r * 128 + c * 16);
+        v_off[g] = uint32_t(r * ldvt * 2 + c * 16);
+    }
+    auto issue = [&](int kt, f16 *ks, f16 *vs) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (k0 + e >= T) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-                    v = make_uint4(w[0], w[1], w[2], w[3]);
-                }
-            }
-            rv[i] = v;
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = (tid >> 3) + 32 * i;
-            *reinterpret_cast<uint4 *>(&Ks[buf][r * 64 + ((ck ^ (r & 7)) << 3)]) = rk[i];
-            // V^T chunk ck holds keys 8 ck .. 8 ck + 7 of 16-key group g = ck >> 1.
-            // LDS chunk 2g + s holds, for lane half s, keys 16g + 4s + {0..3}
-            // then 16g + 8 + 4s + {0..3}.
-            const int lc0 = (ck >> 1) * 2, half = (ck & 1) * 4;
-            *reinterpret_cast<uint2 *>(&Vs[buf][r * 64 + ((lc0 ^ (r & 7)) << 3) + half]) = make_uint2(rv[i].x, rv[i].y);
-            *reinterpret_cast<uint2 *>(&Vs[buf][r * 64 + (((lc0 + 1) ^ (r & 7)) << 3) + half]) = make_uint2(rv[i].z, rv[i].w);
+        for (int g = 0; g < 2; ++g) {
+            load_lds16(rk, ks + (wave * 2 + g) * 8 * 64, k_off[g] + uint32_t(kt) * (KT * 128));
+            load_lds16(rv, vs + (wave * 2 + g) * 8 * 64, v_off[g] + uint32_t(kt) * (KT * 2));
         }
     };
 
@@ -100,23 +121,17 @@ attn_kernel(const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__r
         o[1][r] = 0.f;
     }
     float mrow = -INFINITY, lsum = 0.f;
-
+    const int fsw = swz(l32);  // == swz(row) for every fragment row of this lane
     const int nkt = (T + KT - 1) / KT;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    const int fsw = lane & 7;
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nkt) gload(kt + 1);
 
+    auto step = [&](int kt, const f16 *ks, const f16 *vs) {
         // S^T tiles: rows = keys kt2*32 + 8 (r >> 2) + 4 hh + (r & 3), column = query l32.
         f32x16 s[2];
 #pragma unroll
         for (int kt2 = 0; kt2 < 2; ++kt2) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kt2][r] = 0.f;
-            const f16 *kr = &Ks[cur][(kt2 * 32 + l32) * 64];
+            const f16 *kr = ks + (kt2 * 32 + l32) * 64;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const f16x8 a = *reinterpret_cast<const f16x8 *>(kr + (((kk * 2 + hh) ^ fsw) << 3));
@@ -139,26 +154,35 @@ attn_kernel(const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__r
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt2][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrow, mx);
-        const float alpha = exp2f(mrow - mnew);
-        mrow = mnew;
+        // Lazy rescaling: the reference point mrow only moves when the tile
+        // maximum exceeds it by more than 8 (log2 units), so the running sum
+        // and O are rescaled rarely; probabilities taken against a stale
+        // reference are at most 2^8, well inside fp16 and fp32.  The result
+        // O / l is the same for any reference point.
+        if (mx > mrow + 8.0f) {
+            const float alpha = __builtin_amdgcn_exp2f(mrow - mx);  // 0 on the first tile
+            mrow = mx;
+            lsum *= alpha;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                o[0][r] *= alpha;
+                o[1][r] *= alpha;
+            }
+        }
         float ps = 0.f;
 #pragma unroll
         for (int kt2 = 0; kt2 < 2; ++kt2)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float e = exp2f(s[kt2][r] - mnew);
+                const float e = __builtin_amdgcn_exp2f(s[kt2][r] - mrow);
                 s[kt2][r] = e;
                 ps += e;
             }
-        lsum = lsum * alpha + ps;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            o[0][r] *= alpha;
-            o[1][r] *= alpha;
-        }
+        lsum += ps;
 
-        // O^T[dim][query] += V^T[dim][keys] P^T[keys][query], 16 keys per MFMA.
+        // O^T[dim][query] += V^T[dim][slots] P^T[slots][query], 16 keys per
+        // MFMA: LDS chunk 2 s4 + hh of a V^T row holds exactly the 8 keys lane
+        // half hh has probabilities for.
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
             const int kt2 = s4 >> 1, sg = s4 & 1;
@@ -168,13 +192,26 @@ attn_kernel(const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__r
 #pragma unroll
             for (int ht = 0; ht < 2; ++ht) {
                 const int dim = ht * 32 + l32;
-                const f16x8 va = *reinterpret_cast<const f16x8 *>(&Vs[cur][dim * 64 + (((2 * s4 + hh) ^ fsw) << 3)]);
+                const f16x8 va = *reinterpret_cast<const f16x8 *>(vs + dim * 64 + (((2 * s4 + hh) ^ fsw) << 3));
                 o[ht] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb, o[ht], 0, 0, 0);
             }
         }
+    };
 
-        if (kt + 1 < nkt) sstore(cur ^ 1);
+    // Double-buffered key tiles; the loop is unrolled by two so each LDS
+    // access names its buffer statically.
+    issue(0, Ks0, Vs0);
+#pragma unroll 1
+    for (int kt = 0; kt < nkt; kt += 2) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        if (kt + 1 < nkt) issue(kt + 1, Ks1, Vs1);
+        step(kt, Ks0, Vs0);
+        if (kt + 1 >= nkt) break;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (kt + 2 < nkt) issue(kt + 2, Ks0, Vs0);
+        step(kt + 1, Ks1, Vs1);
     }
 
     lsum += __shfl_xor(lsum, 32);
@@ -198,8 +235,10 @@ attn_kernel(const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__r
 
 const char *attention_check(int batch, int n_head, int T, int ldvt) {
     if (batch < 0 || n_head <= 0 || T <= 0) return "attention: need batch >= 0, n_head > 0, T > 0";
-    if (ldvt < T || ldvt % 8) return "attention: ldvt must be >= T and a multiple of 8";
+    if (ldvt % KT || ldvt < T) return "attention: ldvt must be a multiple of 64 and >= T";
     if (n_head > 65535 || batch > 65535) return "attention: batch and n_head must be < 65536";
+    if (int64_t(ldvt) * 128 >= (int64_t(1) << 31) || int64_t(T) * 128 >= (int64_t(1) << 31))
+        return "attention: T too large";
     return nullptr;
 }
 

@@ -122,6 +122,8 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
+__device__ __forceinline__ uint32_t vt_slot(uint32_t t) { return (t & ~12u) | ((t & 4u) << 1) | ((t & 8u) >> 1); }
+
 // Store 4 consecutive output columns n .. n+3 of row m.
 template <int EPI>
 __device__ __forceinline__ void epi_store4(const GemmP &p, int m, int n, f32x4 v) {
@@ -159,9 +161,17 @@ __device__ __forceinline__ void epi_store4(const GemmP &p, int m, int n, f32x4 v
             f16 *dst = slice == 0 ? p.q : p.k;
             *reinterpret_cast<f16x4 *>(dst + (bh * p.t_div.d + t) * 64 + e) = o;
         } else {
-            f16 *dst = p.vt + (bh * 64 + e) * p.ldvt + t;
+            // V^T key slot: bits 2 and 3 of the key swapped, the order in which
+            // the attention kernel's lanes hold their probabilities.
+            f16 *row = p.vt + (bh * 64 + e) * p.ldvt;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[int64_t(i) * p.ldvt] = (f16)(v[i] + b[i]);
+            for (int i = 0; i < 4; ++i) row[int64_t(i) * p.ldvt + vt_slot(t)] = (f16)(v[i] + b[i]);
+            if (t + 1 == p.t_div.d) {
+                // the last key also clears the slots of keys T .. ldvt-1
+                for (uint32_t u = t + 1; u < uint32_t(p.ldvt); ++u)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) row[int64_t(i) * p.ldvt + vt_slot(u)] = (f16)0.0f;
+            }
         }
     }
 }
@@ -389,7 +399,7 @@ const char *gemm_check(const wenc_gemm_args &a) {
             if (!a.q || !a.k || !a.vt) return "gemm: q, k, vt must be non-null";
             if (a.n_head <= 0 || a.N != 3 * 64 * a.n_head) return "gemm: QKV needs N == 3 * 64 * n_head";
             if (a.T <= 0 || a.T >= (1 << 16) || a.M % a.T) return "gemm: QKV needs 0 < T < 65536 and M % T == 0";
-            if (a.ldvt < a.T) return "gemm: ldvt < T";
+            if (a.ldvt < a.T || a.ldvt % 64) return "gemm: ldvt must be a multiple of 64 and >= T";
             break;
         default:
             return "gemm: unknown epilogue";

@@ -121,7 +121,7 @@ ScratchLayout scratch_layout(const wenc_config &c) {
     const size_t B = c.max_batch, F = c.n_frames, nm = c.n_mels, d = c.d_model, T = c.n_ctx, H = c.n_head,
                  Fd = c.d_ff;
     ScratchLayout s;
-    s.ldvt = int((T + 7) / 8 * 8);
+    s.ldvt = int((T + 63) / 64 * 64);
     Bump b;
     s.melp = b.take(2 * B * (F + 2) * nm);
     s.c1 = b.take(2 * B * (F + 2) * d);
