@@ -69,7 +69,15 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, const f16 *lds, uint32_t 
 __global__ void __launch_bounds__(256)
 attn_kernel(const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__restrict__ vt,
             f16 *__restrict__ ao, int T, int H, int ldvt) {
-    const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // Workgroup ids are dealt round-robin over the 8 XCDs; renumber them so
+    // each XCD gets a contiguous run, which keeps all query tiles of one
+    // (batch, head) -- readers of the same K and V^T -- on one XCD's L2.
+    const int nwg = gridDim.x, bid = blockIdx.x;
+    const int per = nwg >> 3, rem = nwg & 7, xcd = bid & 7, idx = bid >> 3;
+    const int lid = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int nqt = (T + QT - 1) / QT;
+    const int qt = lid % nqt, bhi = lid / nqt;
+    const int h = bhi % H, b = bhi / H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, l32 = lane & 31;
@@ -236,7 +244,7 @@ attn_kernel(const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__r
 const char *attention_check(int batch, int n_head, int T, int ldvt) {
     if (batch < 0 || n_head <= 0 || T <= 0) return "attention: need batch >= 0, n_head > 0, T > 0";
     if (ldvt % KT || ldvt < T) return "attention: ldvt must be a multiple of 64 and >= T";
-    if (n_head > 65535 || batch > 65535) return "attention: batch and n_head must be < 65536";
+    if (int64_t((T + QT - 1) / QT) * n_head * batch >= (int64_t(1) << 31)) return "attention: grid too large";
     if (int64_t(ldvt) * 128 >= (int64_t(1) << 31) || int64_t(T) * 128 >= (int64_t(1) << 31))
         return "attention: T too large";
     return nullptr;
@@ -245,7 +253,7 @@ const char *attention_check(int batch, int n_head, int T, int ldvt) {
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, uint16_t *ao,
                             int batch, int n_head, int T, int ldvt, hipStream_t s) {
     if (batch == 0) return hipSuccess;
-    const dim3 grid((T + QT - 1) / QT, n_head, batch), block(256);
+    const dim3 grid(unsigned((T + QT - 1) / QT) * unsigned(n_head) * unsigned(batch)), block(256);
     attn_kernel<<<grid, block, 0, s>>>(reinterpret_cast<const f16 *>(q), reinterpret_cast<const f16 *>(k),
                                        reinterpret_cast<const f16 *>(vt), reinterpret_cast<f16 *>(ao), T, n_head,
                                        ldvt);

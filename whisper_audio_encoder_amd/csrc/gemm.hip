@@ -176,7 +176,9 @@ __device__ __forceinline__ void epi_store4(const GemmP &p, int m, int n, f32x4 v
     }
 }
 
-template <int BM, int BN, int WM, int WN, int NW, int EPI>
+// TAG only separates otherwise identical instantiations (fc1 from conv1,
+// fc2 from out_proj) so that a kernel trace names each projection.
+template <int BM, int BN, int WM, int WN, int NW, int EPI, int TAG>
 __global__ void __launch_bounds__(NW * 64)
 gemm_kernel(const GemmP p) {
     constexpr int WAVES_N = BN / WN;
@@ -345,20 +347,25 @@ gemm_kernel(const GemmP p) {
     }
 }
 
-template <int BM, int BN, int WM, int WN, int NW>
+template <int BM, int BN, int WM, int WN, int NW, int TAG>
 hipError_t launch_cfg(const GemmP &base, int epi, hipStream_t s) {
     GemmP p = base;
     p.tiles_m = (p.M + BM - 1) / BM;
     p.tiles_n = (p.N + BN - 1) / BN;
     const dim3 grid(p.tiles_m * p.tiles_n), block(NW * 64);
     switch (epi) {
-        case WENC_EPI_GELU_F16: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_GELU_F16><<<grid, block, 0, s>>>(p); break;
-        case WENC_EPI_CONV2: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_CONV2><<<grid, block, 0, s>>>(p); break;
-        case WENC_EPI_RESID: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_RESID><<<grid, block, 0, s>>>(p); break;
-        case WENC_EPI_QKV: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_QKV><<<grid, block, 0, s>>>(p); break;
+        case WENC_EPI_GELU_F16: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_GELU_F16, TAG><<<grid, block, 0, s>>>(p); break;
+        case WENC_EPI_CONV2: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_CONV2, 0><<<grid, block, 0, s>>>(p); break;
+        case WENC_EPI_RESID: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_RESID, TAG><<<grid, block, 0, s>>>(p); break;
+        case WENC_EPI_QKV: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_QKV, 0><<<grid, block, 0, s>>>(p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int NW>
+hipError_t launch_tagged(const GemmP &p, int epi, int tag, hipStream_t s) {
+    return tag ? launch_cfg<BM, BN, WM, WN, NW, 1>(p, epi, s) : launch_cfg<BM, BN, WM, WN, NW, 0>(p, epi, s);
 }
 
 int g_tile_override = -1;  // WENC_GEMM_TILE: 0 = 128x128, 1 = 256x256 x 8 waves, 2 = 256x256 x 4 waves
@@ -407,7 +414,7 @@ const char *gemm_check(const wenc_gemm_args &a) {
     return nullptr;
 }
 
-hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s) {
+hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag) {
     if (a.M == 0) return hipSuccess;
     GemmP p{};
     p.A = reinterpret_cast<const f16 *>(a.A);
@@ -446,9 +453,9 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s) {
         cfg = big >= 448 ? 1 : 0;
     }
     switch (cfg) {
-        case 1: return launch_cfg<256, 256, 128, 64, 8>(p, a.epilogue, s);
-        case 2: return launch_cfg<256, 256, 128, 128, 4>(p, a.epilogue, s);
-        default: return launch_cfg<128, 128, 64, 64, 4>(p, a.epilogue, s);
+        case 1: return launch_tagged<256, 256, 128, 64, 8>(p, a.epilogue, tag, s);
+        case 2: return launch_tagged<256, 256, 128, 128, 4>(p, a.epilogue, tag, s);
+        default: return launch_tagged<128, 128, 64, 64, 4>(p, a.epilogue, tag, s);
     }
 }
 

@@ -9,7 +9,8 @@ namespace wk {
 // Checks the shape/alignment contract of wenc_gemm_args; returns a message
 // or nullptr when the arguments are acceptable.
 const char *gemm_check(const wenc_gemm_args &a);
-hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s);
+// tag 1 selects a separately named copy of the kernel (fc1, fc2).
+hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag = 0);
 
 const char *attention_check(int batch, int n_head, int T, int ldvt);
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, uint16_t *ao,

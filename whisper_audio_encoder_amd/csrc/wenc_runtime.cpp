@@ -353,7 +353,7 @@ int wenc::forward_chunk(const float *mel, int nb, float *out, hipStream_t st, in
         g.N = Fd;
         g.K = d;
         g.epilogue = WENC_EPI_GELU_F16;
-        WENC_TRY(site(WENC_SITE_FC1, st, [&] { return wk::launch_gemm(g, st); }));
+        WENC_TRY(site(WENC_SITE_FC1, st, [&] { return wk::launch_gemm(g, st, 1); }));
         g = wenc_gemm_args{};
         g.A = hb;
         g.a_batch_stride = int64_t(T) * Fd;
@@ -368,7 +368,7 @@ int wenc::forward_chunk(const float *mel, int nb, float *out, hipStream_t st, in
         g.N = d;
         g.K = Fd;
         g.epilogue = WENC_EPI_RESID;
-        WENC_TRY(site(WENC_SITE_FC2, st, [&] { return wk::launch_gemm(g, st); }));
+        WENC_TRY(site(WENC_SITE_FC2, st, [&] { return wk::launch_gemm(g, st, 1); }));
         if (tap == WENC_TAP_BLOCK + l) return copy_x(tap_dst);
     }
 
