@@ -130,7 +130,7 @@ def main(argv=None):
 
     cfg = CONFIGS[a.workload]
     B = a.batch or cfg.batch
-    log(f"[bench] workload {a.workload}: {WORKLOAD_NAMES[a.workload]}, batch {B}")
+    log(f"[bench] workload {a.workload}: {WORKLOAD_NAMES[a.workload]}; running batch {B}")
     mel, params = synth.make_inputs(cfg, batch=B)
     blob = synth.pack_blob(cfg, params)
     enc = wenc.Encoder(cfg, blob, max_batch=B)

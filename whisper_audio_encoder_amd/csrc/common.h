@@ -32,27 +32,27 @@ __device__ __forceinline__ uint32_t divu(uint32_t n, const DivU &v) {
     return uint32_t((uint64_t(n) * v.mul) >> 40);
 }
 
-// erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions (1964),
-// formula 7.1.26 (Hastings' rational approximation): for x >= 0,
-//   erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
-//   t = 1 / (1 + p x),
-// with |error| <= 1.5e-7; odd symmetry gives x < 0.  Two transcendental
-// instructions (reciprocal, exp2) and eight FMA-class operations.
-__device__ __forceinline__ float erf_as(float x) {
-    const float ax = fabsf(x);
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
-    float poly = fmaf(1.061405429f, t, -1.453152027f);
-    poly = fmaf(poly, t, 1.421413741f);
-    poly = fmaf(poly, t, -0.284496736f);
-    poly = fmaf(poly, t, 0.254829592f);
-    poly *= t;
-    const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
-    return copysignf(1.0f - poly * e, x);
-}
-
-// Exact GELU, the error-function form: 0.5 z (1 + erf(z / sqrt 2)).
+// Exact GELU, the error-function form: gelu(z) = z Phi(z), Phi(z) =
+// 0.5 (1 + erf(z / sqrt 2)).  erf comes from Abramowitz & Stegun, Handbook of
+// Mathematical Functions (1964), formula 7.1.26 (Hastings' rational
+// approximation, |error| <= 1.5e-7): for x >= 0,
+//   1 - erf(x) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
+//   t = 1 / (1 + p x).
+// With x = |z| / sqrt 2 and E = 0.5 (1 - erf(x)), Phi(z) = 1 - E for z >= 0
+// and E for z < 0.  The constants below fold the 1/sqrt 2, the 0.5 and the
+// natural-to-base-2 exponent into the coefficients, leaving one reciprocal,
+// one exp2 and ten FMA-class operations.
 __device__ __forceinline__ float gelu_erf(float z) {
-    return 0.5f * z * (1.0f + erf_as(z * 0.70710678118654752f));
+    constexpr float kP = 0.3275911f * 0.70710678118654752f;   // p / sqrt 2
+    constexpr float kE = -0.5f * 1.4426950408889634f;          // -x^2 log2(e) with x^2 = z^2 / 2
+    const float t = __builtin_amdgcn_rcpf(fmaf(kP, fabsf(z), 1.0f));
+    float q = fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
+    q = fmaf(q, t, 0.5f * 1.421413741f);
+    q = fmaf(q, t, 0.5f * -0.284496736f);
+    q = fmaf(q, t, 0.5f * 0.254829592f);
+    const float ex = __builtin_amdgcn_exp2f((z * kE) * z);
+    const float ze = z * (q * t) * ex;  // z * 0.5 (1 - erf(|z| / sqrt 2))
+    return z >= 0.0f ? z - ze : ze;
 }
 
 }  // namespace wk
