@@ -34,25 +34,34 @@ __device__ __forceinline__ uint32_t divu(uint32_t n, const DivU &v) {
 
 // Exact GELU, the error-function form: gelu(z) = z Phi(z), Phi(z) =
 // 0.5 (1 + erf(z / sqrt 2)).  erf comes from Abramowitz & Stegun, Handbook of
-// Mathematical Functions (1964), formula 7.1.26 (Hastings' rational
-// approximation, |error| <= 1.5e-7): for x >= 0,
-//   1 - erf(x) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
-//   t = 1 / (1 + p x).
-// With x = |z| / sqrt 2 and E = 0.5 (1 - erf(x)), Phi(z) = 1 - E for z >= 0
-// and E for z < 0.  The constants below fold the 1/sqrt 2, the 0.5 and the
-// natural-to-base-2 exponent into the coefficients, leaving one reciprocal,
-// one exp2 and ten FMA-class operations.
+// Mathematical Functions (1964), formula 7.1.28 (|error| <= 3e-7): for x >= 0,
+//   1 - erf(x) = (1 + a1 x + a2 x^2 + a3 x^3 + a4 x^4 + a5 x^5 + a6 x^6)^-16.
+// With x = |z| / sqrt 2 and r = 0.5 (1 - erf(x)), Phi(z) = 1 - r for z >= 0
+// and r for z < 0, so in both cases gelu(z) = max(z, 0) - |z| r.  The
+// coefficients below are a_k 2^(-k/2) (the 1/sqrt 2 folded in) times
+// 2^(1/16) (so the 16th power carries the 0.5), leaving six FMAs, four
+// squarings, one reciprocal and one FMA.  In fp32 the result is within
+// 7.1e-7 of the exact GELU everywhere (checked on a dense grid over
+// [-12, 12]); for large |z| the 16th power overflows to +inf, r to 0 and the
+// result to max(z, 0), as it should.
 __device__ __forceinline__ float gelu_erf(float z) {
-    constexpr float kP = 0.3275911f * 0.70710678118654752f;   // p / sqrt 2
-    constexpr float kE = -0.5f * 1.4426950408889634f;          // -x^2 log2(e) with x^2 = z^2 / 2
-    const float t = __builtin_amdgcn_rcpf(fmaf(kP, fabsf(z), 1.0f));
-    float q = fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
-    q = fmaf(q, t, 0.5f * 1.421413741f);
-    q = fmaf(q, t, 0.5f * -0.284496736f);
-    q = fmaf(q, t, 0.5f * 0.254829592f);
-    const float ex = __builtin_amdgcn_exp2f((z * kE) * z);
-    const float ze = z * (q * t) * ex;  // z * 0.5 (1 - erf(|z| / sqrt 2))
-    return z >= 0.0f ? z - ze : ze;
+    const float u = fabsf(z);
+    float q = fmaf(5.621299806e-06f, u, 5.105520904e-05f);
+    q = fmaf(q, u, 3.968613601e-05f);
+    q = fmaf(q, u, 3.422739217e-03f);
+    q = fmaf(q, u, 2.207699791e-02f);
+    q = fmaf(q, u, 5.207516253e-02f);
+    q = fmaf(q, u, 1.044273734e+00f);
+    q *= q;
+    q *= q;
+    q *= q;
+    q *= q;
+    const float r = __builtin_amdgcn_rcpf(q);
+    // max(z, 0) as one instruction: fmaxf would first quiet a signalling NaN
+    // with an extra max.  A NaN z still yields NaN through -u.
+    float pos;
+    asm("v_max_f32_e32 %0, 0, %1" : "=v"(pos) : "v"(z));
+    return fmaf(-u, r, pos);
 }
 
 }  // namespace wk

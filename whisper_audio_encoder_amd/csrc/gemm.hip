@@ -130,25 +130,24 @@ __device__ __forceinline__ uint32_t vt_slot(uint32_t t) { return (t & ~12u) | ((
 // Store 4 consecutive output columns n .. n+3 of row m.
 template <int EPI>
 __device__ __forceinline__ void epi_store4(const GemmP &p, int m, int n, f32x4 v) {
-    const f32x4 b = ld4(p.bias + n);
     if constexpr (EPI == WENC_EPI_GELU_F16) {
         const uint32_t bi = divu(m, p.c_div);
         const uint32_t r = m - bi * p.c_div.d;
         f16 *C = static_cast<f16 *>(p.C) + int64_t(bi) * p.c_bs + int64_t(r + p.c_off) * p.ldc + n;
         f16x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (f16)gelu_erf(v[e] + b[e]);
+        for (int e = 0; e < 4; ++e) o[e] = (f16)gelu_erf(v[e]);
         *reinterpret_cast<f16x4 *>(C) = o;
     } else if constexpr (EPI == WENC_EPI_CONV2) {
         const uint32_t t = m - divu(m, p.pos_div) * p.pos_div.d;
         const f32x4 ps = ld4(p.pos + int64_t(t) * p.N + n);
         f32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = gelu_erf(v[e] + b[e]) + ps[e];
+        for (int e = 0; e < 4; ++e) o[e] = gelu_erf(v[e]) + ps[e];
         *reinterpret_cast<f32x4 *>(static_cast<float *>(p.C) + int64_t(m) * p.ldc + n) = o;
     } else if constexpr (EPI == WENC_EPI_RESID) {
         f32x4 *C = reinterpret_cast<f32x4 *>(static_cast<float *>(p.C) + int64_t(m) * p.ldc + n);
-        *C = *C + v + b;
+        *C = *C + v;
     } else if constexpr (EPI == WENC_EPI_QKV) {
         const int slice = n / p.dmodel;
         const int c = n - slice * p.dmodel;
@@ -160,7 +159,7 @@ __device__ __forceinline__ void epi_store4(const GemmP &p, int m, int n, f32x4 v
             const float sc = slice == 0 ? p.q_scale : 1.0f;
             f16x4 o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = (f16)((v[i] + b[i]) * sc);
+            for (int i = 0; i < 4; ++i) o[i] = (f16)(v[i] * sc);
             f16 *dst = slice == 0 ? p.q : p.k;
             *reinterpret_cast<f16x4 *>(dst + (bh * p.t_div.d + t) * 64 + e) = o;
         } else {
@@ -168,7 +167,7 @@ __device__ __forceinline__ void epi_store4(const GemmP &p, int m, int n, f32x4 v
             // the attention kernel's lanes hold their probabilities.
             f16 *row = p.vt + (bh * 64 + e) * p.ldvt;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) row[int64_t(i) * p.ldvt + vt_slot(t)] = (f16)(v[i] + b[i]);
+            for (int i = 0; i < 4; ++i) row[int64_t(i) * p.ldvt + vt_slot(t)] = (f16)v[i];
             if (t + 1 == p.t_div.d) {
                 // the last key also clears the slots of keys T .. ldvt-1
                 for (uint32_t u = t + 1; u < uint32_t(p.ldvt); ++u)
@@ -244,13 +243,23 @@ gemm_kernel(const GemmP p) {
         }
     };
 
+    // Register r of accumulator tile (i, j) holds row (lane & 31) of the i-th
+    // 32-row block and column 8 (r >> 2) + 4 (lane >> 5) + (r & 3) of the j-th
+    // 32-column block.  Every accumulator starts at its column's bias, so the
+    // epilogues add none.
+    const int hh = lane >> 5;
     f32x16 acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int g = 0; g < 4; ++g) {
+            const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * hh;
+            const f32x4 b = n < p.N ? ld4(p.bias + n) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] = b[e];
+        }
 
     // Fragment reads: lane supplies row (lane & 31) of a 32-row tile and k
     // values 8 (lane >> 5) .. +7 of the current 16-wide slice.  Two fragment
@@ -337,9 +346,7 @@ gemm_kernel(const GemmP p) {
         if (kt + 1 < nk) step(kt + 1, smem1, smem0);
     }
 
-    // Epilogue: register r of tile (i, j) holds row m = (lane & 31) of the
-    // i-th 32-row block and column 8 (r >> 2) + 4 (lane >> 5) + (r & 3).
-    const int hh = lane >> 5;
+    // Epilogue, in the register layout described at the accumulators.
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int m = m0 + wm * WM + i * 32 + frow;
