@@ -103,6 +103,19 @@ int wenc_load(wenc_t *h, const void *blob, size_t nbytes);
  * Enqueued on `stream`; no host synchronisation. */
 int wenc_forward(wenc_t *h, const float *mel, int32_t batch, float *out, void *stream);
 
+/* Shortened-context forward (drafts; whisper README, section Serving:
+ * a draft encodes the audio plus 5 s, at least 10 s, instead of the full
+ * 30 s window, as whisper.cpp's audio_ctx does).  The same encoder runs over
+ * 2 * n_ctx frames and adds the FIRST n_ctx rows of the stored position
+ * table; attention spans those n_ctx positions only.
+ *   mel: device, fp32 [batch][2 * n_ctx][n_mels];
+ *   out: device, fp32 [batch][n_ctx][d_model].
+ * 1 <= n_ctx <= the configured n_ctx, else WENC_EINVAL before any launch;
+ * n_ctx equal to the configured one is wenc_forward.  Windows are chunked by
+ * what the scratch holds at this length (more than max_batch when n_ctx is
+ * shorter).  Enqueued on `stream`; no host synchronisation. */
+int wenc_forward_ctx(wenc_t *h, const float *mel, int32_t batch, int32_t n_ctx, float *out, void *stream);
+
 /* Release the handle and its device memory.  NULL-safe.  Synchronises the
  * device first so no enqueued work still uses the memory. */
 void wenc_destroy(wenc_t *h);

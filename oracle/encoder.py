@@ -139,15 +139,24 @@ def encode(mel, params: dict, n_layer: int, n_head: int, eps: float = 1e-5,
            final_ln: bool = True, taps: bool = False):
     """Encoder forward of ONE window.
 
-    mel: [n_frames, n_mels] (3000 x n_mels).  params: the canonical parameter
-    dict (conv1_w, conv1_b, conv2_w, conv2_b, pos, l{i}.<field>, lnf_g,
-    lnf_b).  Returns the [n_frames // 2, d] memory in fp64, or with
-    ``taps=True`` a dict holding the stage outputs ``c1`` (after conv1+GELU),
-    ``x0`` (after conv2+GELU+positions), ``blocks`` (x after each block) and
-    ``out``.
+    mel: [n_frames, n_mels] (3000 x n_mels for a full 30 s window).  params:
+    the canonical parameter dict (conv1_w, conv1_b, conv2_w, conv2_b, pos,
+    l{i}.<field>, lnf_g, lnf_b).  Returns the [n_frames // 2, d] memory in
+    fp64, or with ``taps=True`` a dict holding the stage outputs ``c1``
+    (after conv1+GELU), ``x0`` (after conv2+GELU+positions), ``blocks`` (x
+    after each block) and ``out``.
+
+    A shorter mel is a shortened-context window (drafts: whisper
+    README, section Serving: the audio plus 5 s instead of 30 s, as
+    whisper.cpp's audio_ctx).  Reading: the same layers run over T =
+    n_frames // 2 positions, position t adds row t of the stored table (its
+    first T rows), and attention spans those T positions.
     """
     c1 = gelu(conv1d(mel, params["conv1_w"], params["conv1_b"], stride=1))
-    x = gelu(conv1d(c1, params["conv2_w"], params["conv2_b"], stride=2)) + _f64(params["pos"])
+    stem = gelu(conv1d(c1, params["conv2_w"], params["conv2_b"], stride=2))
+    pos = _f64(params["pos"])
+    assert stem.shape[0] <= pos.shape[0], "more positions than the stored table holds"
+    x = stem + pos[:stem.shape[0]]
     x0 = x
     blocks = []
     for li in range(n_layer):

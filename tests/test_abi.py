@@ -62,6 +62,7 @@ def test_null_handles():
     assert L.wenc_load(None, None, 0) == wenc.WENC_EINVAL
     assert L.wenc_forward(None, None, 1, None, None) == wenc.WENC_EINVAL
     assert L.wenc_forward_tap(None, None, 1, 0, None, None) == wenc.WENC_EINVAL
+    assert L.wenc_forward_ctx(None, None, 1, 500, None, None) == wenc.WENC_EINVAL
     assert L.wenc_profile(None, 0) == wenc.WENC_EINVAL
     assert L.wenc_create(None, None) == wenc.WENC_EINVAL
     assert wenc.wenc_last_error(None) != ""

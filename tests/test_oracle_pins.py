@@ -257,6 +257,50 @@ def test_encoder_taps_consistent():
     np.testing.assert_array_equal(t["out"], oracle.encode(mel, params, cfg.n_layer, cfg.n_head))
 
 
+# ------------------------------------------------- shortened context (drafts)
+def test_draft_stem_is_prefix_of_full_stem():
+    """A draft of 2T' frames of the same audio gives the full window's stem
+    rows 0 .. T'-2 (conv is local and positions are aligned at the start);
+    row T'-1 differs, because frame 2T' is the draft's zero padding."""
+    cfg = _small_cfg(n_layer=0)
+    mel, params = _small_inputs(cfg)
+    full = oracle.encode(mel, params, 0, cfg.n_head, taps=True)["x0"]
+    for Td in (1, 2, 7, 13):
+        draft = oracle.encode(mel[:2 * Td], params, 0, cfg.n_head, taps=True)["x0"]
+        assert draft.shape == (Td, cfg.d_model)
+        np.testing.assert_allclose(draft[:Td - 1], full[:Td - 1], rtol=0, atol=1e-12)
+        assert np.abs(draft[Td - 1] - full[Td - 1]).max() > 1e-4
+
+
+def test_draft_positions_are_leading_rows():
+    """With the stem silenced (zero conv weights and biases, gelu(0) = 0) and
+    no blocks, a draft's output is exactly rows 0 .. T'-1 of the table."""
+    cfg = _small_cfg(n_layer=0)
+    mel, params = _small_inputs(cfg)
+    for f in ("conv1_w", "conv1_b", "conv2_w", "conv2_b"):
+        params[f] = np.zeros_like(params[f])
+    out = oracle.encode(mel[:14], params, 0, cfg.n_head, final_ln=False)
+    np.testing.assert_array_equal(out, params["pos"][:7])
+
+
+def test_draft_matches_torch_layers():
+    """Blocks over T' < n_ctx positions against torch's float64 layers."""
+    cfg = _small_cfg()
+    mel, params = _small_inputs(cfg, scale_attn=6.0)
+    got = oracle.encode(mel[:22], params, cfg.n_layer, cfg.n_head, cfg.ln_eps)
+    ref = torch_encode(mel[:22], params, cfg.n_layer, cfg.n_head, cfg.ln_eps)
+    assert got.shape == (11, cfg.d_model)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-10)
+
+
+def test_draft_longer_than_table_is_refused():
+    cfg = _small_cfg(n_layer=0)
+    mel, params = _small_inputs(cfg)
+    longer = np.concatenate([mel, mel[:4]])
+    with pytest.raises(AssertionError):
+        oracle.encode(longer, params, 0, cfg.n_head)
+
+
 # --------------------------------------------------------------- shapes (P-f)
 def test_family_golden_matches_configs():
     fam = {r[0]: tuple(map(int, r[1:])) for r in read_golden("whisper_family.txt")}

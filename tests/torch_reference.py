@@ -43,7 +43,8 @@ def torch_encode(mel, params, n_layer, n_head, eps=1e-5, final_ln=True):
     with torch.no_grad():
         c1 = F.gelu(F.conv1d(x, _t(params["conv1_w"]), _t(params["conv1_b"]), stride=1, padding=1))
         c2 = F.gelu(F.conv1d(c1, _t(params["conv2_w"]), _t(params["conv2_b"]), stride=2, padding=1))
-        h = c2[0].T + _t(params["pos"])
+        h = c2[0].T
+        h = h + _t(params["pos"])[:h.shape[0]]  # a shortened window uses the leading rows
         for li in range(n_layer):
             p = {k.split(".", 1)[1]: v for k, v in params.items() if k.startswith(f"l{li}.")}
             d_ff = p["fc1_w"].shape[0]

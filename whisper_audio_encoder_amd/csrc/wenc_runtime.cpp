@@ -8,6 +8,7 @@
 // out_proj, LN2, fc1, fc2, and the final LN (3 + 7 L + 1 launches per chunk).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -223,7 +224,8 @@ struct wenc {
         return WENC_OK;
     }
 
-    int forward_chunk(const float *mel, int nb, float *out, hipStream_t st, int tap, void *tap_dst);
+    int forward_chunk(const float *mel, int nb, int T, float *out, hipStream_t st, int tap, void *tap_dst);
+    int chunk_cap(int T) const;
 };
 
 #define WENC_TRY(expr)                 \
@@ -232,10 +234,22 @@ struct wenc {
         if (rc_ != WENC_OK) return rc_; \
     } while (0)
 
-int wenc::forward_chunk(const float *mel, int nb, float *out, hipStream_t st, int tap, void *tap_dst) {
+// Windows of T positions (2T frames) one pass through the scratch can hold.
+// The buffers are sized for max_batch windows of the configured n_ctx and
+// packed densely at any T <= n_ctx, so a shortened context fits more windows.
+int wenc::chunk_cap(int T) const {
+    const int64_t B = cfg.max_batch, Tc = cfg.n_ctx, Fc = cfg.n_frames, F = 2 * int64_t(T);
+    const int64_t ldvt = (T + 63) / 64 * 64;
+    int64_t cap = std::min({B * Tc / T, B * (Fc + 2) / (F + 2), B * sl.ldvt / ldvt});
+    cap = std::min(cap, ((int64_t(1) << 24) - 1) / F);  // row indices of the conv GEMMs stay < 2^24
+    return int(std::max<int64_t>(cap, 1));
+}
+
+int wenc::forward_chunk(const float *mel, int nb, int T, float *out, hipStream_t st, int tap, void *tap_dst) {
     const wenc_config &c = cfg;
-    const int F = c.n_frames, T = c.n_ctx, nm = c.n_mels, d = c.d_model, H = c.n_head, Fd = c.d_ff;
+    const int F = 2 * T, nm = c.n_mels, d = c.d_model, H = c.n_head, Fd = c.d_ff;
     const int M = nb * T;
+    const int ldvt = (T + 63) / 64 * 64;
     uint16_t *melp = S<uint16_t>(sl.melp), *c1 = S<uint16_t>(sl.c1), *xn = S<uint16_t>(sl.xn);
     uint16_t *q = S<uint16_t>(sl.q), *k = S<uint16_t>(sl.k), *vt = S<uint16_t>(sl.vt);
     uint16_t *ao = S<uint16_t>(sl.ao), *hb = S<uint16_t>(sl.hbuf);
@@ -311,14 +325,14 @@ int wenc::forward_chunk(const float *mel, int nb, float *out, hipStream_t st, in
         g.vt = vt;
         g.T = T;
         g.n_head = H;
-        g.ldvt = sl.ldvt;
+        g.ldvt = ldvt;
         g.q_scale = q_scale;
         g.M = M;
         g.N = 3 * d;
         g.K = d;
         g.epilogue = WENC_EPI_QKV;
         WENC_TRY(site(WENC_SITE_QKV, st, [&] { return wk::launch_gemm(g, st); }));
-        WENC_TRY(site(WENC_SITE_ATTN, st, [&] { return wk::launch_attention(q, k, vt, ao, nb, H, T, sl.ldvt, st); }));
+        WENC_TRY(site(WENC_SITE_ATTN, st, [&] { return wk::launch_attention(q, k, vt, ao, nb, H, T, ldvt, st); }));
         g = wenc_gemm_args{};
         g.A = ao;
         g.a_batch_stride = int64_t(T) * d;
@@ -503,38 +517,46 @@ int wenc_load(wenc_t *h, const void *blob, size_t nbytes) {
     return WENC_OK;
 }
 
-static int forward_impl(wenc_t *h, const float *mel, int32_t batch, float *out, void *stream, int tap, void *tap_dst) {
+static int forward_impl(wenc_t *h, const float *mel, int32_t batch, int32_t n_ctx, float *out, void *stream, int tap,
+                        void *tap_dst) {
     if (!h) return fail(nullptr, WENC_EINVAL, "wenc_forward: handle is NULL");
     if (!h->loaded) return fail(&h->err, WENC_ESTATE, "wenc_forward: no weights loaded (call wenc_load first)");
     if (batch < 0) return fail(&h->err, WENC_EINVAL, "wenc_forward: batch %d < 0", batch);
+    const wenc_config &c = h->cfg;
+    if (n_ctx < 1 || n_ctx > c.n_ctx)
+        return fail(&h->err, WENC_EINVAL, "wenc_forward_ctx: n_ctx %d outside [1, %d]", n_ctx, c.n_ctx);
     if (batch == 0) return WENC_OK;
     if (!mel) return fail(&h->err, WENC_EINVAL, "wenc_forward: mel is NULL");
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const wenc_config &c = h->cfg;
     if (tap >= 0) {
         if (!tap_dst) return fail(&h->err, WENC_EINVAL, "wenc_forward_tap: dst is NULL");
         if (tap > WENC_TAP_BLOCK + c.n_layer - 1)
             return fail(&h->err, WENC_EINVAL, "wenc_forward_tap: tap %d out of range", tap);
         if (batch > c.max_batch)
             return fail(&h->err, WENC_EINVAL, "wenc_forward_tap: batch %d > max_batch %d", batch, c.max_batch);
-        return h->forward_chunk(mel, batch, nullptr, st, tap, tap_dst);
+        return h->forward_chunk(mel, batch, n_ctx, nullptr, st, tap, tap_dst);
     }
     if (!out) return fail(&h->err, WENC_EINVAL, "wenc_forward: out is NULL");
-    for (int b0 = 0; b0 < batch; b0 += c.max_batch) {
-        const int nb = batch - b0 < c.max_batch ? batch - b0 : c.max_batch;
-        WENC_TRY(h->forward_chunk(mel + size_t(b0) * c.n_frames * c.n_mels, nb, out + size_t(b0) * c.n_ctx * c.d_model, st,
-                                  -1, nullptr));
+    const int cap = h->chunk_cap(n_ctx);
+    for (int b0 = 0; b0 < batch; b0 += cap) {
+        const int nb = batch - b0 < cap ? batch - b0 : cap;
+        WENC_TRY(h->forward_chunk(mel + size_t(b0) * 2 * n_ctx * c.n_mels, nb, n_ctx,
+                                  out + size_t(b0) * n_ctx * c.d_model, st, -1, nullptr));
     }
     return WENC_OK;
 }
 
 int wenc_forward(wenc_t *h, const float *mel, int32_t batch, float *out, void *stream) {
-    return forward_impl(h, mel, batch, out, stream, -1, nullptr);
+    return forward_impl(h, mel, batch, h ? h->cfg.n_ctx : 1, out, stream, -1, nullptr);
+}
+
+int wenc_forward_ctx(wenc_t *h, const float *mel, int32_t batch, int32_t n_ctx, float *out, void *stream) {
+    return forward_impl(h, mel, batch, n_ctx, out, stream, -1, nullptr);
 }
 
 int wenc_forward_tap(wenc_t *h, const float *mel, int32_t batch, int32_t tap, void *dst, void *stream) {
     if (h && tap < 0) return fail(&h->err, WENC_EINVAL, "wenc_forward_tap: tap %d < 0", tap);
-    return forward_impl(h, mel, batch, nullptr, stream, tap, dst);
+    return forward_impl(h, mel, batch, h ? h->cfg.n_ctx : 1, nullptr, stream, tap, dst);
 }
 
 void wenc_destroy(wenc_t *h) {

@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.wenc_load.restype = ctypes.c_int
     L.wenc_forward.argtypes = [vp, vp, i32, vp, vp]
     L.wenc_forward.restype = ctypes.c_int
+    L.wenc_forward_ctx.argtypes = [vp, vp, i32, i32, vp, vp]
+    L.wenc_forward_ctx.restype = ctypes.c_int
     L.wenc_forward_tap.argtypes = [vp, vp, i32, i32, vp, vp]
     L.wenc_forward_tap.restype = ctypes.c_int
     L.wenc_destroy.argtypes = [vp]
@@ -153,6 +155,10 @@ def wenc_forward(h, mel: torch.Tensor, batch: int, out: torch.Tensor, stream=Non
     _check(lib().wenc_forward(h, _ptr(mel), batch, _ptr(out), _stream(stream)), h)
 
 
+def wenc_forward_ctx(h, mel: torch.Tensor, batch: int, n_ctx: int, out: torch.Tensor, stream=None) -> None:
+    _check(lib().wenc_forward_ctx(h, _ptr(mel), batch, n_ctx, _ptr(out), _stream(stream)), h)
+
+
 def wenc_forward_tap(h, mel: torch.Tensor, batch: int, tap: int, dst: torch.Tensor, stream=None) -> None:
     _check(lib().wenc_forward_tap(h, _ptr(mel), batch, tap, _ptr(dst), _stream(stream)), h)
 
@@ -200,23 +206,31 @@ class Encoder:
             self.h = None
             raise
 
-    def _check_mel(self, mel: torch.Tensor):
+    def _check_mel(self, mel: torch.Tensor, n_frames: int | None = None):
         c = self.cfg
+        n_frames = c.n_frames if n_frames is None else n_frames
         if not (mel.is_cuda and mel.dtype == torch.float32 and mel.is_contiguous()):
             raise ValueError("mel must be a contiguous fp32 device tensor")
-        if mel.dim() != 3 or mel.shape[1:] != (c.n_frames, c.n_mels):
-            raise ValueError(f"mel must be [batch, {c.n_frames}, {c.n_mels}], got {tuple(mel.shape)}")
+        if mel.dim() != 3 or mel.shape[1:] != (n_frames, c.n_mels):
+            raise ValueError(f"mel must be [batch, {n_frames}, {c.n_mels}], got {tuple(mel.shape)}")
 
-    def forward(self, mel: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-        self._check_mel(mel)
+    def forward(self, mel: torch.Tensor, out: torch.Tensor | None = None, stream=None,
+                n_ctx: int | None = None) -> torch.Tensor:
+        """Encode full windows, or with ``n_ctx`` a shortened context (drafts):
+        mel [batch, 2 n_ctx, n_mels] -> out [batch, n_ctx, d_model]."""
         c = self.cfg
+        T = c.n_ctx if n_ctx is None else n_ctx
+        self._check_mel(mel, 2 * T)
         B = mel.shape[0]
         if out is None:
-            out = torch.empty((B, c.n_ctx, c.d_model), dtype=torch.float32, device=mel.device)
+            out = torch.empty((B, T, c.d_model), dtype=torch.float32, device=mel.device)
         elif not (out.is_cuda and out.dtype == torch.float32 and out.is_contiguous()
-                  and tuple(out.shape) == (B, c.n_ctx, c.d_model)):
-            raise ValueError("out must be a contiguous fp32 device tensor [batch, n_ctx, d_model]")
-        wenc_forward(self.h, mel, B, out, stream)
+                  and tuple(out.shape) == (B, T, c.d_model)):
+            raise ValueError(f"out must be a contiguous fp32 device tensor [batch, {T}, d_model]")
+        if n_ctx is None:
+            wenc_forward(self.h, mel, B, out, stream)
+        else:
+            wenc_forward_ctx(self.h, mel, B, n_ctx, out, stream)
         return out
 
     def tap(self, mel: torch.Tensor, tap: int, stream=None) -> torch.Tensor:
