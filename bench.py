@@ -49,6 +49,9 @@ def site_work(cfg, B):
         "ln2": ("hbm", M * d * (4.0 + 2.0)),
         "lnf": ("hbm", M * d * (4.0 + 4.0)),
         "ingest": ("hbm", B * F * nm * 4.0 + B * (F + 2) * nm * 2.0),
+        # cross K/V, per decoder layer: [B T, d] x [d, 2d]; the conversion reads fp32, writes fp16
+        "xkv": ("mfma", 2.0 * M * 2 * d * d),
+        "xcvt": ("hbm", M * d * (4.0 + 2.0)),
     }
 
 
@@ -56,7 +59,7 @@ PROFILES = os.path.join(HERE, "profiles")
 CSRC = "whisper_audio_encoder_amd/csrc/"
 SITE_SOURCES = {"attn": ("attention.hip", "common.h"), "ln1": ("layernorm.hip", "common.h"),
                 "ln2": ("layernorm.hip", "common.h"), "lnf": ("layernorm.hip", "common.h"),
-                "ingest": ("layernorm.hip", "common.h")}
+                "ingest": ("layernorm.hip", "common.h"), "xcvt": ("layernorm.hip", "common.h")}
 
 
 def kernel_source_hash(site):
@@ -105,6 +108,35 @@ def cpu_baseline(cfg, mel, params, budget_s=30.0):
             "sample": f"one full window (batch item 0) of the same workload, fp64 numpy/OpenBLAS, {dt:.1f} s"}
 
 
+def time_cross(enc, model, memory, n_dec, steps):
+    """The decoder's cross-attention K/V of n_dec layers from the encoder
+    output, timed like the forward (events on the stream, after a warm-up)."""
+    import torch
+    from whisper_audio_encoder_amd import synth, wenc
+    enc.load_cross(synth.pack_cross_blob(model, synth.make_cross_params(model, n_dec), n_dec), n_dec)
+    B, T, d = memory.shape
+    xk = torch.empty((n_dec, B, T, d), dtype=torch.float16, device=memory.device)
+    xv = torch.empty_like(xk)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        wenc.wenc_prepare_cross(enc.h, memory, B, T, xk, xv)
+    wenc.wenc_profile(enc.h, 1 << wenc.SITES.index("xkv"))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        wenc.wenc_prepare_cross(enc.h, memory, B, T, xk, xv)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kv_ms, kv_n = wenc.wenc_profile_read(enc.h)["xkv"]
+    wenc.wenc_profile(enc.h, 0)
+    flops = 2.0 * B * T * 2 * d * d * n_dec
+    log(f"[bench] cross K/V, {n_dec} decoder layers: {ms:.3f} ms per call, {flops / ms / 1e9:.1f} TFLOP/s")
+    return {"n_dec_layer": n_dec, "ms_per_call": ms, "tflops": flops / ms / 1e9,
+            "gemm_avg_launch_ms": kv_ms / max(kv_n, 1)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +147,8 @@ def main(argv=None):
     ap.add_argument("--n-ctx", type=int, default=None,
                     help="shortened context (drafts): encode 2*N_CTX frames per window with the full model")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cross", type=int, default=None, metavar="N_DEC",
+                    help="also time the cross-attention K/V projection of N_DEC decoder layers from the output")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
     a = ap.parse_args(argv)
@@ -192,6 +226,10 @@ def main(argv=None):
     roof["avg_launch_ms"] = avg_s * 1e3
     roof["launches"] = d_n
 
+    cross = None
+    if a.cross:
+        cross = time_cross(enc, model, out, a.cross, a.steps)
+
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on one window ...")
@@ -220,6 +258,7 @@ def main(argv=None):
         "site_ms_per_step": {s: warm[s][0] / n_warm for s in wenc.SITES if warm[s][1]},
         "roofline": roof,
         "cpu_baseline": cpu,
+        **({"cross_kv": cross} if cross else {}),
         "host": platform.node(),
     }
     enc.close()

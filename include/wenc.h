@@ -125,6 +125,35 @@ void wenc_destroy(wenc_t *h);
 const char *wenc_last_error(const wenc_t *h);
 
 /* ------------------------------------------------------------------------
+ * Cross-attention K/V of the decoder, projected from the encoder memory once
+ * per clip (whisper 0.9.0 API page, wh_prepare_cross: the encoder does not
+ * change while a clip is transcribed, so its K and V are not recomputed per
+ * token; model.nu: per decoder layer x_wk has no bias, x_wv has x_bv).
+ * ---------------------------------------------------------------------- */
+
+/* Byte size of the cross-attention blob for n_dec_layer decoder layers of
+ * width d_model: per layer, in this order, x_wk [d][d], x_wv [d][d], x_bv [d],
+ * all fp16 (IEEE binary16, little-endian), matrices [out][in] row-major.
+ * 0 for an invalid config or n_dec_layer <= 0. */
+size_t wenc_cross_nbytes(const wenc_config *cfg, int32_t n_dec_layer);
+
+/* Copy a HOST cross blob into a device arena of the handle (replacing any
+ * earlier one), stacked per layer as [x_wk; x_wv] fp16 [2d][d] with bias
+ * [0; x_bv] fp32.  nbytes must equal wenc_cross_nbytes.  Synchronous. */
+int wenc_load_cross(wenc_t *h, int32_t n_dec_layer, const void *blob, size_t nbytes);
+
+/* For every loaded decoder layer l and window b < batch:
+ *   xk[l][b] = memory[b] . x_wk[l]^T,  xv[l][b] = memory[b] . x_wv[l]^T + x_bv[l].
+ *   memory: device fp32 [batch][n_ctx][d_model] (wenc_forward's or
+ *           wenc_forward_ctx's out), rounded to fp16 once before use;
+ *   xk, xv: device fp16 [n_dec_layer][batch][n_ctx][d_model] each.
+ * 1 <= n_ctx <= the configured n_ctx.  WENC_ESTATE before wenc_load_cross.
+ * Uses the handle's scratch (no forward may overlap it).  Enqueued on
+ * `stream`; no host synchronisation. */
+int wenc_prepare_cross(wenc_t *h, const float *memory, int32_t batch, int32_t n_ctx, void *xk, void *xv,
+                       void *stream);
+
+/* ------------------------------------------------------------------------
  * Stage taps and kernel entry points.  They expose each step of the path in
  * isolation so that it can be compared with an independent implementation
  * (the CKE page: every kernel has its own parity oracle).  All pointers are
@@ -150,7 +179,8 @@ enum {
     WENC_EPI_GELU_F16 = 0, /* C fp16 = gelu(acc + bias)                       (fc1, conv1) */
     WENC_EPI_CONV2 = 1,    /* C fp32 = gelu(acc + bias) + pos[m % pos_rows]   (conv2)      */
     WENC_EPI_RESID = 2,    /* C fp32 += acc + bias                            (out_proj, fc2) */
-    WENC_EPI_QKV = 3       /* q, k, v^T scatter, see wenc_gemm_args           (qkv)        */
+    WENC_EPI_QKV = 3,      /* q, k, v^T scatter, see wenc_gemm_args           (qkv)        */
+    WENC_EPI_KV = 4        /* C, C2 fp16 = acc + bias, split at n_split       (cross K/V)  */
 };
 
 /* GEMM arguments.  Row m of A starts at
@@ -166,7 +196,10 @@ enum {
  * [batch][n_head][64][ldvt] fp16 with m = b * T + t, where key t of a row
  * sits at slot t with bits 2 and 3 swapped (the order the attention kernel
  * consumes) and the slots of keys T .. ldvt-1 are written with zeros; the q
- * slice is multiplied by q_scale after its bias.  Requires K % 8 == 0,
+ * slice is multiplied by q_scale after its bias.
+ * KV: columns [0, n_split) go to C and [n_split, N) to C2 (column
+ * n - n_split), both fp16 with row m at m * ldc; 0 < n_split <= N,
+ * n_split % 4 == 0, ldc >= max(n_split, N - n_split).  Requires K % 8 == 0,
  * lda % 8 == 0, ldw % 8 == 0, a_batch_stride % 8 == 0, N, ldc and
  * c_batch_stride multiples of 4, ldvt a multiple of 64, M < 2^24. */
 typedef struct wenc_gemm_args {
@@ -178,6 +211,7 @@ typedef struct wenc_gemm_args {
     uint16_t *q; uint16_t *k; uint16_t *vt; int32_t T; int32_t n_head; int32_t ldvt; float q_scale;
     int32_t M, N, K;
     int32_t epilogue;
+    uint16_t *C2; int32_t n_split;        /* KV only                            */
 } wenc_gemm_args;
 int wenc_k_gemm(const wenc_gemm_args *args, void *stream);
 
@@ -192,14 +226,15 @@ int wenc_k_gemm(const wenc_gemm_args *args, void *stream);
 int wenc_k_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, uint16_t *ao,
                      int32_t batch, int32_t n_head, int32_t T, int32_t ldvt, void *stream);
 
-/* Per-launch timing of wenc_forward with HIP events recorded on the caller's
+/* Per-launch timing of wenc_forward and wenc_prepare_cross with HIP events recorded on the caller's
  * stream around the launches whose site bit is set in `site_mask`
  * (bit s = 1 << WENC_SITE_*); 0 turns it off.  Events are read, and cleared,
  * by wenc_profile_read (which synchronises on them). */
 enum {
     WENC_SITE_INGEST = 0, WENC_SITE_CONV1 = 1, WENC_SITE_CONV2 = 2, WENC_SITE_LN1 = 3,
     WENC_SITE_QKV = 4, WENC_SITE_ATTN = 5, WENC_SITE_OPROJ = 6, WENC_SITE_LN2 = 7,
-    WENC_SITE_FC1 = 8, WENC_SITE_FC2 = 9, WENC_SITE_LNF = 10, WENC_N_SITES = 11
+    WENC_SITE_FC1 = 8, WENC_SITE_FC2 = 9, WENC_SITE_LNF = 10, WENC_SITE_XCVT = 11,
+    WENC_SITE_XKV = 12, WENC_N_SITES = 13
 };
 int wenc_profile(wenc_t *h, uint32_t site_mask);
 /* ms_total[s] and launches[s] for s < WENC_N_SITES (arrays of that length). */

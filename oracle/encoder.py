@@ -167,3 +167,16 @@ def encode(mel, params: dict, n_layer: int, n_head: int, eps: float = 1e-5,
     if taps:
         return {"c1": c1, "x0": x0, "blocks": blocks, "out": out}
     return out
+
+
+def cross_kv(memory, x_wk, x_wv, x_bv):
+    """Cross-attention keys and values of one decoder layer, projected from
+    the encoder memory once per clip (whisper 0.9.0 API page, wh_prepare_cross;
+    model.nu: x_wk has no bias, x_wv has x_bv; CKE page, "The Decoder": the
+    memory is frozen, so its K/V are computed once and cached).
+
+    memory: [T, d] (the encoder output).  Returns (K, V), each [T, d]:
+    K = memory . x_wk^T, V = memory . x_wv^T + x_bv, in fp64.
+    """
+    m = _f64(memory)
+    return m @ _f64(x_wk).T, m @ _f64(x_wv).T + _f64(x_bv)

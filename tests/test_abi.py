@@ -63,6 +63,8 @@ def test_null_handles():
     assert L.wenc_forward(None, None, 1, None, None) == wenc.WENC_EINVAL
     assert L.wenc_forward_tap(None, None, 1, 0, None, None) == wenc.WENC_EINVAL
     assert L.wenc_forward_ctx(None, None, 1, 500, None, None) == wenc.WENC_EINVAL
+    assert L.wenc_load_cross(None, 1, None, 0) == wenc.WENC_EINVAL
+    assert L.wenc_prepare_cross(None, None, 1, 1500, None, None, None) == wenc.WENC_EINVAL
     assert L.wenc_profile(None, 0) == wenc.WENC_EINVAL
     assert L.wenc_create(None, None) == wenc.WENC_EINVAL
     assert wenc.wenc_last_error(None) != ""
@@ -94,3 +96,14 @@ def test_create_without_device_reports_enodev():
     h = ctypes.c_void_p()
     assert wenc.lib().wenc_create(ctypes.byref(c), ctypes.byref(h)) == wenc.WENC_ENODEV
     assert "no HIP device" in wenc.wenc_last_error()
+
+
+def test_cross_blob_size():
+    """Per decoder layer: x_wk [d][d], x_wv [d][d], x_bv [d] in fp16."""
+    for name, n in (("c0", 1), ("c4", 32)):
+        cfg = CONFIGS[name]
+        d = cfg.d_model
+        want = 2 * n * (2 * d * d + d)
+        assert wenc.wenc_cross_nbytes(wenc.make_config(cfg), n) == want
+        assert synth.pack_cross_blob(cfg, synth.make_cross_params(cfg, n), n).nbytes == want
+    assert wenc.wenc_cross_nbytes(wenc.make_config(CONFIGS["c0"]), 0) == 0

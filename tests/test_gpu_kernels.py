@@ -92,6 +92,9 @@ def _gemm(A, W, bias, epi, M, N, K, **kw):
     a.n_head = kw.get("n_head", 0)
     a.ldvt = kw.get("ldvt", 0)
     a.q_scale = kw.get("q_scale", 1.0)
+    C2 = kw.get("C2")
+    a.C2 = C2.data_ptr() if C2 is not None else None
+    a.n_split = kw.get("n_split", 0)
     a.M, a.N, a.K, a.epilogue = M, N, K, epi
     wenc.wenc_k_gemm(a)
 

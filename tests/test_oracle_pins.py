@@ -301,6 +301,47 @@ def test_draft_longer_than_table_is_refused():
         oracle.encode(longer, params, 0, cfg.n_head)
 
 
+# ------------------------------------------- cross-attention K/V (decoder side)
+def test_cross_kv_brute_force():
+    """Pure-Python sums at a tiny, non-square-friendly size."""
+    rng = np.random.default_rng(21)
+    T, d = 5, 6
+    m = rng.standard_normal((T, d))
+    wk, wv, bv = rng.standard_normal((d, d)), rng.standard_normal((d, d)), rng.standard_normal(d)
+    K, V = oracle.cross_kv(m, wk, wv, bv)
+    for t in range(T):
+        for o in range(d):
+            k_ref = sum(float(m[t, c]) * float(wk[o, c]) for c in range(d))
+            v_ref = float(bv[o]) + sum(float(m[t, c]) * float(wv[o, c]) for c in range(d))
+            assert abs(K[t, o] - k_ref) < 1e-12 and abs(V[t, o] - v_ref) < 1e-12
+
+
+def test_cross_kv_matches_torch_linear_and_identity():
+    rng = np.random.default_rng(22)
+    m = rng.standard_normal((37, 64))
+    wk, wv, bv = rng.standard_normal((64, 64)), rng.standard_normal((64, 64)), rng.standard_normal(64)
+    K, V = oracle.cross_kv(m, wk, wv, bv)
+    tm = torch.from_numpy(m)
+    np.testing.assert_allclose(K, F.linear(tm, torch.from_numpy(wk)).numpy(), atol=1e-12)
+    np.testing.assert_allclose(V, F.linear(tm, torch.from_numpy(wv), torch.from_numpy(bv)).numpy(), atol=1e-12)
+    eye = np.eye(64)
+    K, V = oracle.cross_kv(m, eye, eye, bv)
+    np.testing.assert_array_equal(K, m)
+    np.testing.assert_allclose(V, m + bv, atol=0)
+
+
+def test_cross_k_bias_would_be_unobservable():
+    """x_wk has no bias; a bias c would add q.c to every score of a query,
+    which the softmax over keys cancels: the zero-bias reading loses nothing."""
+    rng = np.random.default_rng(23)
+    m = rng.standard_normal((30, 64))
+    wk = rng.standard_normal((64, 64)) * 0.1
+    K, _ = oracle.cross_kv(m, wk, wk, np.zeros(64))
+    q = rng.standard_normal((3, 64))
+    c = rng.standard_normal(64)
+    np.testing.assert_allclose(oracle.softmax_rows(q @ (K + c).T), oracle.softmax_rows(q @ K.T), atol=1e-12)
+
+
 # --------------------------------------------------------------- shapes (P-f)
 def test_family_golden_matches_configs():
     fam = {r[0]: tuple(map(int, r[1:])) for r in read_golden("whisper_family.txt")}

@@ -53,6 +53,8 @@ struct GemmP {
     const float *pos;
     DivU pos_div;
     f16 *q, *k, *vt;
+    f16 *C2;
+    int n_split;
     DivU t_div;
     int H, ldvt, dmodel;
     float q_scale;
@@ -148,6 +150,13 @@ __device__ __forceinline__ void epi_store4(const GemmP &p, int m, int n, f32x4 v
     } else if constexpr (EPI == WENC_EPI_RESID) {
         f32x4 *C = reinterpret_cast<f32x4 *>(static_cast<float *>(p.C) + int64_t(m) * p.ldc + n);
         *C = *C + v;
+    } else if constexpr (EPI == WENC_EPI_KV) {
+        const bool hi = n >= p.n_split;  // a run of 4 never straddles n_split (both multiples of 4)
+        f16 *C = (hi ? p.C2 : static_cast<f16 *>(p.C)) + int64_t(m) * p.ldc + (hi ? n - p.n_split : n);
+        f16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (f16)v[e];
+        *reinterpret_cast<f16x4 *>(C) = o;
     } else if constexpr (EPI == WENC_EPI_QKV) {
         const int slice = n / p.dmodel;
         const int c = n - slice * p.dmodel;
@@ -375,6 +384,7 @@ hipError_t launch_cfg(const GemmP &base, int epi, hipStream_t s) {
         case WENC_EPI_CONV2: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_CONV2, 0><<<grid, block, 0, s>>>(p); break;
         case WENC_EPI_RESID: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_RESID, TAG><<<grid, block, 0, s>>>(p); break;
         case WENC_EPI_QKV: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_QKV, 0><<<grid, block, 0, s>>>(p); break;
+        case WENC_EPI_KV: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_KV, 0><<<grid, block, 0, s>>>(p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -425,6 +435,12 @@ const char *gemm_check(const wenc_gemm_args &a) {
             if (a.T <= 0 || a.T >= (1 << 16) || a.M % a.T) return "gemm: QKV needs 0 < T < 65536 and M % T == 0";
             if (a.ldvt < a.T || a.ldvt % 64) return "gemm: ldvt must be a multiple of 64 and >= T";
             break;
+        case WENC_EPI_KV:
+            if (!a.C) return "gemm: C is null";
+            if (a.n_split <= 0 || a.n_split > a.N || a.n_split % 4) return "gemm: KV needs 0 < n_split <= N, n_split % 4 == 0";
+            if (a.n_split < a.N && !a.C2) return "gemm: C2 is null";
+            if (a.ldc < a.n_split || a.ldc < a.N - a.n_split) return "gemm: ldc < max(n_split, N - n_split)";
+            break;
         default:
             return "gemm: unknown epilogue";
     }
@@ -451,6 +467,8 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag) {
     p.q = reinterpret_cast<f16 *>(a.q);
     p.k = reinterpret_cast<f16 *>(a.k);
     p.vt = reinterpret_cast<f16 *>(a.vt);
+    p.C2 = reinterpret_cast<f16 *>(a.C2);
+    p.n_split = a.n_split;
     p.t_div = make_divu(a.T > 0 ? a.T : 1);
     p.H = a.n_head;
     p.ldvt = a.ldvt;

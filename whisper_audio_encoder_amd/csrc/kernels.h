@@ -25,4 +25,7 @@ hipError_t launch_layernorm(const float *x, const float *g, const float *b, void
 hipError_t launch_ingest(const float *mel, uint16_t *melp, uint16_t *c1, int B, int F, int nm, int d,
                          hipStream_t s);
 
+// y fp16 [n] = x fp32 [n] rounded to nearest even; n % 4 == 0, 16-byte aligned.
+hipError_t launch_to_f16(const float *x, uint16_t *y, int64_t n, hipStream_t s);
+
 }  // namespace wk

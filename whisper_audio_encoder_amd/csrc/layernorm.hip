@@ -116,6 +116,16 @@ ingest_kernel(const float *__restrict__ mel, f16 *__restrict__ melp, f16 *__rest
     }
 }
 
+// y = fp16(x), round to nearest even, four values per thread (n4 groups).
+__global__ void __launch_bounds__(256)
+to_f16_kernel(const float4 *__restrict__ x, f16x4 *__restrict__ y, int64_t n4) {
+    const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const float4 v = x[i];
+        y[i] = f16x4{(f16)v.x, (f16)v.y, (f16)v.z, (f16)v.w};
+    }
+}
+
 }  // namespace
 
 const char *layernorm_check(int rows, int d) {
@@ -148,6 +158,16 @@ hipError_t launch_ingest(const float *mel, uint16_t *melp, uint16_t *c1, int B, 
     if (blocks > 4096) blocks = 4096;
     ingest_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, s>>>(mel, reinterpret_cast<f16 *>(melp),
                                                              reinterpret_cast<f16 *>(c1), B, F, nm, d);
+    return hipGetLastError();
+}
+
+hipError_t launch_to_f16(const float *x, uint16_t *y, int64_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    if (n % 4) return hipErrorInvalidValue;
+    int64_t blocks = (n / 4 + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    to_f16_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, s>>>(reinterpret_cast<const float4 *>(x),
+                                                             reinterpret_cast<f16x4 *>(y), n / 4);
     return hipGetLastError();
 }
 

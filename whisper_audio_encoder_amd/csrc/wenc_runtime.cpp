@@ -172,6 +172,9 @@ struct wenc {
     int device = 0;
     char *warena = nullptr;
     char *sarena = nullptr;
+    char *xarena = nullptr;  // cross-attention K/V weights (wenc_load_cross)
+    int n_dec = 0;
+    size_t x_stride = 0;     // bytes per decoder layer in xarena: W_kv fp16 [2d][d], then bias fp32 [2d]
     WeightLayout wl;
     ScratchLayout sl;
     bool loaded = false;
@@ -559,6 +562,100 @@ int wenc_forward_tap(wenc_t *h, const float *mel, int32_t batch, int32_t tap, vo
     return forward_impl(h, mel, batch, h ? h->cfg.n_ctx : 1, nullptr, stream, tap, dst);
 }
 
+size_t wenc_cross_nbytes(const wenc_config *cfg, int32_t n_dec_layer) {
+    if (config_error(cfg) || n_dec_layer <= 0 || n_dec_layer > 4096) return 0;
+    const size_t d = cfg->d_model;
+    return 2 * size_t(n_dec_layer) * (2 * d * d + d);
+}
+
+int wenc_load_cross(wenc_t *h, int32_t n_dec_layer, const void *blob, size_t nbytes) {
+    if (!h) return fail(nullptr, WENC_EINVAL, "wenc_load_cross: handle is NULL");
+    if (!blob) return fail(&h->err, WENC_EINVAL, "wenc_load_cross: blob is NULL");
+    const size_t want = wenc_cross_nbytes(&h->cfg, n_dec_layer);
+    if (want == 0) return fail(&h->err, WENC_EINVAL, "wenc_load_cross: n_dec_layer %d outside [1, 4096]", n_dec_layer);
+    if (nbytes != want)
+        return fail(&h->err, WENC_EINVAL, "wenc_load_cross: blob is %zu bytes, expected exactly %zu", nbytes, want);
+    const size_t d = h->cfg.d_model;
+    const size_t stride = (4 * d * d + 8 * d + 255) & ~size_t(255);
+    std::vector<char> host(stride * n_dec_layer, 0);
+    const uint16_t *src = static_cast<const uint16_t *>(blob);
+    for (int l = 0; l < n_dec_layer; ++l) {
+        char *dst = host.data() + l * stride;
+        std::memcpy(dst, src, 2 * d * d * 2);  // x_wk then x_wv: rows [0, d) and [d, 2d) of W_kv
+        src += 2 * d * d;
+        float *bias = reinterpret_cast<float *>(dst + 4 * d * d);  // [0; x_bv]: x_wk has no bias
+        for (size_t i = 0; i < d; ++i) bias[d + i] = half_to_float(src[i]);
+        src += d;
+    }
+    hipError_t e = hipSetDevice(h->device);
+    if (e != hipSuccess) return fail(&h->err, WENC_EHIP, "wenc_load_cross: hipSetDevice: %s", hipGetErrorString(e));
+    if (h->xarena) {
+        hipDeviceSynchronize();  // no enqueued work may still read the old weights
+        hipFree(h->xarena);
+        h->xarena = nullptr;
+        h->n_dec = 0;
+    }
+    e = hipMalloc(reinterpret_cast<void **>(&h->xarena), host.size());
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        size_t fr = 0, tot = 0;
+        hipMemGetInfo(&fr, &tot);
+        h->xarena = nullptr;
+        return fail(&h->err, WENC_ENOMEM, "wenc_load_cross: cannot allocate %zu bytes (device has %zu free of %zu)",
+                    host.size(), fr, tot);
+    }
+    e = hipMemcpy(h->xarena, host.data(), host.size(), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(&h->err, WENC_EHIP, "wenc_load_cross: upload failed: %s", hipGetErrorString(e));
+    h->n_dec = n_dec_layer;
+    h->x_stride = stride;
+    return WENC_OK;
+}
+
+int wenc_prepare_cross(wenc_t *h, const float *memory, int32_t batch, int32_t n_ctx, void *xk, void *xv,
+                       void *stream) {
+    if (!h) return fail(nullptr, WENC_EINVAL, "wenc_prepare_cross: handle is NULL");
+    if (!h->xarena) return fail(&h->err, WENC_ESTATE, "wenc_prepare_cross: no cross weights (call wenc_load_cross first)");
+    const wenc_config &c = h->cfg;
+    if (batch < 0) return fail(&h->err, WENC_EINVAL, "wenc_prepare_cross: batch %d < 0", batch);
+    if (n_ctx < 1 || n_ctx > c.n_ctx)
+        return fail(&h->err, WENC_EINVAL, "wenc_prepare_cross: n_ctx %d outside [1, %d]", n_ctx, c.n_ctx);
+    if (batch == 0) return WENC_OK;
+    if (!memory || !xk || !xv) return fail(&h->err, WENC_EINVAL, "wenc_prepare_cross: memory, xk and xv must be non-null");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int d = c.d_model, T = n_ctx;
+    const int cap = h->chunk_cap(T);
+    uint16_t *mh = h->S<uint16_t>(h->sl.xn);  // the memory in fp16, [nb * T][d]
+    for (int b0 = 0; b0 < batch; b0 += cap) {
+        const int nb = batch - b0 < cap ? batch - b0 : cap;
+        const int64_t rows = int64_t(nb) * T;
+        WENC_TRY(h->site(WENC_SITE_XCVT, st, [&] {
+            return wk::launch_to_f16(memory + size_t(b0) * T * d, mh, rows * d, st);
+        }));
+        for (int l = 0; l < h->n_dec; ++l) {
+            const char *lw = h->xarena + l * h->x_stride;
+            const size_t off = (size_t(l) * batch + b0) * size_t(T) * d;
+            wenc_gemm_args g{};
+            g.A = mh;
+            g.a_batch_stride = int64_t(T) * d;
+            g.a_rows_per_batch = T;
+            g.lda = d;
+            g.W = reinterpret_cast<const uint16_t *>(lw);
+            g.ldw = d;
+            g.bias = reinterpret_cast<const float *>(lw + size_t(4) * d * d);
+            g.C = static_cast<uint16_t *>(xk) + off;
+            g.C2 = static_cast<uint16_t *>(xv) + off;
+            g.n_split = d;
+            g.ldc = d;
+            g.M = int(rows);
+            g.N = 2 * d;
+            g.K = d;
+            g.epilogue = WENC_EPI_KV;
+            WENC_TRY(h->site(WENC_SITE_XKV, st, [&] { return wk::launch_gemm(g, st); }));
+        }
+    }
+    return WENC_OK;
+}
+
 void wenc_destroy(wenc_t *h) {
     if (!h) return;
     hipDeviceSynchronize();
@@ -569,6 +666,7 @@ void wenc_destroy(wenc_t *h) {
     for (auto e : h->event_pool) hipEventDestroy(e);
     if (h->warena) hipFree(h->warena);
     if (h->sarena) hipFree(h->sarena);
+    if (h->xarena) hipFree(h->xarena);
     delete h;
 }
 

@@ -107,3 +107,35 @@ def pack_blob(cfg: EncoderConfig, params: dict) -> np.ndarray:
 
 def layer_params(params: dict, li: int) -> dict:
     return {f: params[f"l{li}.{f}"] for f in LAYER_FIELDS}
+
+
+# Cross-attention K/V weights of the decoder layers (the fields of the
+# Whisper struct on the whisper 0.9.0 API page that project the encoder
+# memory: x_wk without a bias, x_wv with x_bv), drawn from their own stream
+# (PCG64 seeded with seed + 7919) so that the encoder's draws are unchanged.
+CROSS_FIELDS = ("x_wk", "x_wv", "x_bv")
+CROSS_SEED_OFFSET = 7919
+
+
+def cross_shapes(d: int, n_dec_layer: int):
+    out = []
+    for li in range(n_dec_layer):
+        out += [(f"d{li}.x_wk", (d, d)), (f"d{li}.x_wv", (d, d)), (f"d{li}.x_bv", (d,))]
+    return out
+
+
+def make_cross_params(cfg: EncoderConfig, n_dec_layer: int, seed: int | None = None) -> dict:
+    """N(0, 0.02) draws rounded to fp16, in blob order."""
+    rng = np.random.default_rng((cfg.seed if seed is None else seed) + CROSS_SEED_OFFSET)
+    return {name: (rng.standard_normal(size=shape, dtype=np.float32) * np.float32(0.02)).astype(np.float16)
+            for name, shape in cross_shapes(cfg.d_model, n_dec_layer)}
+
+
+def pack_cross_blob(cfg: EncoderConfig, cross: dict, n_dec_layer: int) -> np.ndarray:
+    parts = []
+    for name, shape in cross_shapes(cfg.d_model, n_dec_layer):
+        a = np.asarray(cross[name])
+        if a.shape != tuple(shape) or a.dtype != np.float16:
+            raise ValueError(f"{name}: expected fp16 {shape}, got {a.dtype} {a.shape}")
+        parts.append(np.ascontiguousarray(a).reshape(-1))
+    return np.concatenate(parts).view(np.uint8)

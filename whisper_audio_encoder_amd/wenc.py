@@ -25,8 +25,8 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 WENC_OK, WENC_EINVAL, WENC_ENOMEM, WENC_ENODEV, WENC_ESTATE, WENC_EHIP = 0, -1, -2, -3, -4, -5
 WENC_TAP_C1, WENC_TAP_STEM, WENC_TAP_BLOCK = 0, 1, 2
-WENC_EPI_GELU_F16, WENC_EPI_CONV2, WENC_EPI_RESID, WENC_EPI_QKV = 0, 1, 2, 3
-SITES = ("ingest", "conv1", "conv2", "ln1", "qkv", "attn", "oproj", "ln2", "fc1", "fc2", "lnf")
+WENC_EPI_GELU_F16, WENC_EPI_CONV2, WENC_EPI_RESID, WENC_EPI_QKV, WENC_EPI_KV = 0, 1, 2, 3, 4
+SITES = ("ingest", "conv1", "conv2", "ln1", "qkv", "attn", "oproj", "ln2", "fc1", "fc2", "lnf", "xcvt", "xkv")
 N_SITES = len(SITES)
 
 
@@ -55,6 +55,7 @@ class wenc_gemm_args(ctypes.Structure):
         ("n_head", ctypes.c_int32), ("ldvt", ctypes.c_int32), ("q_scale", ctypes.c_float),
         ("M", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
         ("epilogue", ctypes.c_int32),
+        ("C2", ctypes.c_void_p), ("n_split", ctypes.c_int32),
     ]
 
 
@@ -79,6 +80,12 @@ def lib() -> ctypes.CDLL:
     L.wenc_load.restype = ctypes.c_int
     L.wenc_forward.argtypes = [vp, vp, i32, vp, vp]
     L.wenc_forward.restype = ctypes.c_int
+    L.wenc_cross_nbytes.argtypes = [cfgp, i32]
+    L.wenc_cross_nbytes.restype = sz
+    L.wenc_load_cross.argtypes = [vp, i32, vp, sz]
+    L.wenc_load_cross.restype = ctypes.c_int
+    L.wenc_prepare_cross.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+    L.wenc_prepare_cross.restype = ctypes.c_int
     L.wenc_forward_ctx.argtypes = [vp, vp, i32, i32, vp, vp]
     L.wenc_forward_ctx.restype = ctypes.c_int
     L.wenc_forward_tap.argtypes = [vp, vp, i32, i32, vp, vp]
@@ -159,6 +166,20 @@ def wenc_forward_ctx(h, mel: torch.Tensor, batch: int, n_ctx: int, out: torch.Te
     _check(lib().wenc_forward_ctx(h, _ptr(mel), batch, n_ctx, _ptr(out), _stream(stream)), h)
 
 
+def wenc_cross_nbytes(cfg: wenc_config, n_dec_layer: int) -> int:
+    return lib().wenc_cross_nbytes(ctypes.byref(cfg), n_dec_layer)
+
+
+def wenc_load_cross(h, n_dec_layer: int, blob: np.ndarray) -> None:
+    blob = np.ascontiguousarray(blob)
+    _check(lib().wenc_load_cross(h, n_dec_layer, blob.ctypes.data, blob.nbytes), h)
+
+
+def wenc_prepare_cross(h, memory: torch.Tensor, batch: int, n_ctx: int, xk: torch.Tensor, xv: torch.Tensor,
+                       stream=None) -> None:
+    _check(lib().wenc_prepare_cross(h, _ptr(memory), batch, n_ctx, _ptr(xk), _ptr(xv), _stream(stream)), h)
+
+
 def wenc_forward_tap(h, mel: torch.Tensor, batch: int, tap: int, dst: torch.Tensor, stream=None) -> None:
     _check(lib().wenc_forward_tap(h, _ptr(mel), batch, tap, _ptr(dst), _stream(stream)), h)
 
@@ -232,6 +253,26 @@ class Encoder:
         else:
             wenc_forward_ctx(self.h, mel, B, n_ctx, out, stream)
         return out
+
+    def load_cross(self, blob: np.ndarray, n_dec_layer: int) -> None:
+        """Load the decoder layers' cross-attention K/V weights (x_wk, x_wv, x_bv)."""
+        wenc_load_cross(self.h, n_dec_layer, blob)
+        self.n_dec_layer = n_dec_layer
+
+    def prepare_cross(self, memory: torch.Tensor, stream=None):
+        """Cross-attention K and V of every loaded decoder layer from the
+        encoder memory [batch, n_ctx, d_model] fp32: two fp16 tensors
+        [n_dec_layer, batch, n_ctx, d_model]."""
+        c = self.cfg
+        if not (memory.is_cuda and memory.dtype == torch.float32 and memory.is_contiguous()
+                and memory.dim() == 3 and memory.shape[2] == c.d_model):
+            raise ValueError("memory must be a contiguous fp32 device tensor [batch, n_ctx, d_model]")
+        B, T = memory.shape[0], memory.shape[1]
+        n = getattr(self, "n_dec_layer", 0)
+        xk = torch.empty((n, B, T, c.d_model), dtype=torch.float16, device=memory.device)
+        xv = torch.empty_like(xk)
+        wenc_prepare_cross(self.h, memory, B, T, xk, xv, stream)
+        return xk, xv
 
     def tap(self, mel: torch.Tensor, tap: int, stream=None) -> torch.Tensor:
         self._check_mel(mel)
