@@ -15,3 +15,4 @@ from .encoder import (  # noqa: F401
     mha,
     softmax_rows,
 )
+from .frontend import hann_periodic, log_mel, mel_filters, stft_power  # noqa: F401,E402

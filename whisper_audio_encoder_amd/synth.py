@@ -139,3 +139,38 @@ def pack_cross_blob(cfg: EncoderConfig, cross: dict, n_dec_layer: int) -> np.nda
             raise ValueError(f"{name}: expected fp16 {shape}, got {a.dtype} {a.shape}")
         parts.append(np.ascontiguousarray(a).reshape(-1))
     return np.concatenate(parts).view(np.uint8)
+
+
+# Synthetic 16 kHz audio for the log-mel frontend, standing in for the pages'
+# clips (an 11-s recording padded to the fixed 30-s window of 480,000
+# samples: CKE page, "The Frontend").  Voiced stretches: a harmonic series on
+# a fundamental drawn in [90, 250] Hz with 1/h amplitudes, under a slow random
+# envelope, plus N(0, 0.003) noise; silent gaps; then exact zeros after
+# `speech_s` seconds.  Clipped to [-1, 1], fp32.  Own stream: seed + 104729.
+AUDIO_SEED_OFFSET = 104729
+
+
+def make_audio(batch: int, n_samples: int = 480000, seed: int = 0, speech_s: float = 11.0,
+               sr: int = 16000) -> np.ndarray:
+    rng = np.random.default_rng(seed + AUDIO_SEED_OFFSET)
+    out = np.zeros((batch, n_samples), dtype=np.float64)
+    n_speech = min(n_samples, int(speech_s * sr))
+    t = np.arange(n_speech) / sr
+    for b in range(batch):
+        sig = np.zeros(n_speech)
+        pos = 0
+        while pos < n_speech:
+            seg = int(rng.uniform(0.15, 0.6) * sr)
+            end = min(n_speech, pos + seg)
+            if rng.uniform() < 0.75:  # voiced
+                f0 = rng.uniform(90.0, 250.0)
+                tt = t[pos:end]
+                env = np.sin(np.pi * (tt - tt[0]) / max(tt[-1] - tt[0], 1e-3)) ** 2 * rng.uniform(0.05, 0.5)
+                for h in range(1, 16):
+                    if h * f0 >= sr / 2:
+                        break
+                    sig[pos:end] += env / h * np.sin(2 * np.pi * h * f0 * tt + rng.uniform(0, 2 * np.pi))
+            pos = end
+        sig += rng.normal(0.0, 0.003, n_speech)
+        out[b, :n_speech] = sig
+    return np.clip(out, -1.0, 1.0).astype(np.float32)
