@@ -52,6 +52,8 @@ def site_work(cfg, B):
         # cross K/V, per decoder layer: [B T, d] x [d, 2d]; the conversion reads fp32, writes fp16
         "xkv": ("mfma", 2.0 * M * 2 * d * d),
         "xcvt": ("hbm", M * d * (4.0 + 2.0)),
+        # log-mel: per frame, the DFT as a contraction (400 samples x 201 bins x (cos, sin)) and the filters
+        "mel": ("mfma", 2.0 * B * F * (2 * 400 * 201 + 201 * nm)),
     }
 
 
@@ -108,6 +110,36 @@ def cpu_baseline(cfg, mel, params, budget_s=30.0):
             "sample": f"one full window (batch item 0) of the same workload, fp64 numpy/OpenBLAS, {dt:.1f} s"}
 
 
+PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix
+
+
+def time_frontend(enc, model, B, steps):
+    """wenc_log_mel over B synthetic windows, timed with events on the stream."""
+    import torch
+    from whisper_audio_encoder_amd import synth, wenc
+    audio = torch.from_numpy(synth.make_audio(B, n_samples=160 * model.n_frames, seed=model.seed)).to("cuda:0")
+    mel = torch.empty((B, model.n_frames, model.n_mels), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        enc.log_mel(audio, mel)
+    wenc.wenc_profile(enc.h, 1 << wenc.SITES.index("mel"))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        enc.log_mel(audio, mel)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    wenc.wenc_profile(enc.h, 0)
+    flops = 2.0 * B * model.n_frames * (2 * 400 * 201 + 201 * model.n_mels)
+    tf = flops / ms / 1e9
+    log(f"[bench] log-mel, {B} windows: {ms:.3f} ms per call, {tf:.1f} TFLOP/s (DFT as a contraction, fp32)")
+    return {"windows": B, "ms_per_call": ms, "windows_per_s": B / (ms * 1e-3),
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_F32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / PEAK_F32_MFMA_TFLOPS}}
+
+
 def time_cross(enc, model, memory, n_dec, steps):
     """The decoder's cross-attention K/V of n_dec layers from the encoder
     output, timed like the forward (events on the stream, after a warm-up)."""
@@ -147,6 +179,8 @@ def main(argv=None):
     ap.add_argument("--n-ctx", type=int, default=None,
                     help="shortened context (drafts): encode 2*N_CTX frames per window with the full model")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--frontend", action="store_true",
+                    help="also time the log-mel frontend on the same number of synthetic 30-s windows")
     ap.add_argument("--cross", type=int, default=None, metavar="N_DEC",
                     help="also time the cross-attention K/V projection of N_DEC decoder layers from the output")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -226,6 +260,7 @@ def main(argv=None):
     roof["avg_launch_ms"] = avg_s * 1e3
     roof["launches"] = d_n
 
+    frontend = time_frontend(enc, model, B, a.steps) if a.frontend else None
     cross = None
     if a.cross:
         cross = time_cross(enc, model, out, a.cross, a.steps)
@@ -259,6 +294,7 @@ def main(argv=None):
         "roofline": roof,
         "cpu_baseline": cpu,
         **({"cross_kv": cross} if cross else {}),
+        **({"log_mel": frontend} if frontend else {}),
         "host": platform.node(),
     }
     enc.close()

@@ -124,6 +124,19 @@ void wenc_destroy(wenc_t *h);
  * in this thread when h is NULL).  Never NULL; "" when there is none. */
 const char *wenc_last_error(const wenc_t *h);
 
+/* Log-mel spectrogram of whole windows, the encoder's input (CKE page, "The
+ * Frontend: Sound Becomes A Tensor"): STFT power with n_fft 400, hop 160, a
+ * periodic Hann window and reflect padding (frames centred, the last STFT
+ * frame dropped); n_mels area-normalised triangles on the Slaney mel scale
+ * over 0 .. 8 kHz; log10 of max(power, 1e-10); clamp at the window's maximum
+ * minus 8 (-80 dB); (x + 4) / 4.  All in fp32.
+ *   audio: device fp32 [batch][160 * n_frames], 16 kHz mono, already padded
+ *          or cut to the window (480,000 samples for 3000 frames);
+ *   mel:   device fp32 [batch][n_frames][n_mels], wenc_forward's input.
+ * Needs n_mels a multiple of 8, <= 128 (Whisper uses 80 and 128), else
+ * WENC_EINVAL.  batch > max_batch runs in chunks.  Enqueued on `stream`. */
+int wenc_log_mel(wenc_t *h, const float *audio, int32_t batch, float *mel, void *stream);
+
 /* ------------------------------------------------------------------------
  * Cross-attention K/V of the decoder, projected from the encoder memory once
  * per clip (whisper 0.9.0 API page, wh_prepare_cross: the encoder does not
@@ -226,15 +239,16 @@ int wenc_k_gemm(const wenc_gemm_args *args, void *stream);
 int wenc_k_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, uint16_t *ao,
                      int32_t batch, int32_t n_head, int32_t T, int32_t ldvt, void *stream);
 
-/* Per-launch timing of wenc_forward and wenc_prepare_cross with HIP events recorded on the caller's
- * stream around the launches whose site bit is set in `site_mask`
+/* Per-launch timing of wenc_forward, wenc_prepare_cross and wenc_log_mel
+ * with HIP events recorded on the caller's stream around the launches whose
+ * site bit is set in `site_mask`
  * (bit s = 1 << WENC_SITE_*); 0 turns it off.  Events are read, and cleared,
  * by wenc_profile_read (which synchronises on them). */
 enum {
     WENC_SITE_INGEST = 0, WENC_SITE_CONV1 = 1, WENC_SITE_CONV2 = 2, WENC_SITE_LN1 = 3,
     WENC_SITE_QKV = 4, WENC_SITE_ATTN = 5, WENC_SITE_OPROJ = 6, WENC_SITE_LN2 = 7,
     WENC_SITE_FC1 = 8, WENC_SITE_FC2 = 9, WENC_SITE_LNF = 10, WENC_SITE_XCVT = 11,
-    WENC_SITE_XKV = 12, WENC_N_SITES = 13
+    WENC_SITE_XKV = 12, WENC_SITE_MEL = 13, WENC_N_SITES = 14
 };
 int wenc_profile(wenc_t *h, uint32_t site_mask);
 /* ms_total[s] and launches[s] for s < WENC_N_SITES (arrays of that length). */

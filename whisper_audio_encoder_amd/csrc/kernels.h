@@ -25,6 +25,15 @@ hipError_t launch_layernorm(const float *x, const float *g, const float *b, void
 hipError_t launch_ingest(const float *mel, uint16_t *melp, uint16_t *c1, int B, int F, int nm, int d,
                          hipStream_t s);
 
+// Log-mel frontend: audio fp32 [batch][160 n_frames] -> out fp32
+// [batch][n_frames][n_mels].  tab: [400] (cos, -sin) pairs of 2 pi i / 400;
+// win: [400] periodic Hann; filt: [32 ceil(n_mels / 32)][224] fp32 Slaney
+// filters, zero beyond bin 200 and filter n_mels - 1; blkmax: [batch][tiles].
+int logmel_tiles(int n_frames);
+const char *logmel_check(int batch, int n_frames, int n_mels);
+hipError_t launch_logmel(const float *audio, int batch, int n_frames, const float *tab, const float *win,
+                         const float *filt, int n_mels, float *out, float *blkmax, hipStream_t s);
+
 // y fp16 [n] = x fp32 [n] rounded to nearest even; n % 4 == 0, 16-byte aligned.
 hipError_t launch_to_f16(const float *x, uint16_t *y, int64_t n, hipStream_t s);
 

@@ -160,6 +160,48 @@ size_t blob_halves(const wenc_config &c) {
     return d * nm * 3 + d + d * d * 3 + d + T * d + c.n_layer * layer + 2 * d;
 }
 
+// Slaney's auditory-toolbox mel scale: linear (200/3 Hz per mel) below 1 kHz,
+// logarithmic above (27 mels per factor 6.4).
+double hz_to_mel_slaney(double f) { return f < 1000.0 ? f / (200.0 / 3.0) : 15.0 + std::log(f / 1000.0) / (std::log(6.4) / 27.0); }
+double mel_to_hz_slaney(double m) { return m < 15.0 ? m * (200.0 / 3.0) : 1000.0 * std::exp((std::log(6.4) / 27.0) * (m - 15.0)); }
+
+// Constant tables of the log-mel frontend (CKE page, "The Frontend"), in fp64
+// rounded to fp32: (cos, -sin) of 2 pi i / 400; the periodic Hann window
+// 0.5 - 0.5 cos(2 pi i / 400); and n_mels triangles whose corners are
+// evenly spaced in Slaney mels from 0 Hz to 8 kHz, each scaled by 2 / (its
+// width in Hz) (unit area), sampled at the 201 bins k * 40 Hz and stored
+// [32 ceil(n_mels / 32)][224] with zero padding.
+struct FrontendTables {
+    std::vector<float> tab, win, filt;
+};
+
+FrontendTables frontend_tables(int n_mels) {
+    FrontendTables t;
+    const double pi = 3.14159265358979323846;
+    t.tab.resize(800);
+    t.win.resize(400);
+    for (int i = 0; i < 400; ++i) {
+        const double a = 2.0 * pi * i / 400.0;
+        t.tab[2 * i] = float(std::cos(a));
+        t.tab[2 * i + 1] = float(-std::sin(a));
+        t.win[i] = float(0.5 - 0.5 * std::cos(a));
+    }
+    const int rows = (n_mels + 31) / 32 * 32;
+    t.filt.assign(size_t(rows) * 224, 0.0f);
+    const double top = hz_to_mel_slaney(8000.0);
+    std::vector<double> c(n_mels + 2);
+    for (int i = 0; i < n_mels + 2; ++i) c[i] = mel_to_hz_slaney(top * i / (n_mels + 1));
+    for (int i = 0; i < n_mels; ++i)
+        for (int k = 0; k <= 200; ++k) {
+            const double hz = 40.0 * k;
+            const double rise = (hz - c[i]) / (c[i + 1] - c[i]);
+            const double fall = (c[i + 2] - hz) / (c[i + 2] - c[i + 1]);
+            const double w = std::max(0.0, std::min(rise, fall)) * 2.0 / (c[i + 2] - c[i]);
+            t.filt[size_t(i) * 224 + k] = float(w);
+        }
+    return t;
+}
+
 struct ProfRec {
     int site;
     hipEvent_t e0, e1;
@@ -173,6 +215,8 @@ struct wenc {
     char *warena = nullptr;
     char *sarena = nullptr;
     char *xarena = nullptr;  // cross-attention K/V weights (wenc_load_cross)
+    char *farena = nullptr;  // log-mel tables and per-tile maxima (when n_mels suits the frontend)
+    size_t f_win = 0, f_filt = 0, f_blk = 0;
     int n_dec = 0;
     size_t x_stride = 0;     // bytes per decoder layer in xarena: W_kv fp16 [2d][d], then bias fp32 [2d]
     WeightLayout wl;
@@ -451,9 +495,26 @@ int wenc_create(const wenc_config *cfg, wenc_t **out) {
         e = hipMemset(h->sarena, poison && poison[0] == '1' ? 0xff : 0, h->sl.total);
         if (e != hipSuccess) rc = fail(nullptr, WENC_EHIP, "wenc_create: hipMemset: %s", hipGetErrorString(e));
     }
+    if (rc == WENC_OK && !wk::logmel_check(1, cfg->n_frames, cfg->n_mels)) {
+        const FrontendTables t = frontend_tables(cfg->n_mels);
+        Bump fb;
+        const size_t tab = fb.take(4 * t.tab.size());
+        h->f_win = fb.take(4 * t.win.size());
+        h->f_filt = fb.take(4 * t.filt.size());
+        h->f_blk = fb.take(4 * size_t(cfg->max_batch) * wk::logmel_tiles(cfg->n_frames));
+        rc = alloc(&h->farena, fb.off, "log-mel tables");
+        if (rc == WENC_OK) {
+            e = hipMemcpy(h->farena + tab, t.tab.data(), 4 * t.tab.size(), hipMemcpyHostToDevice);
+            if (e == hipSuccess) e = hipMemcpy(h->farena + h->f_win, t.win.data(), 4 * t.win.size(), hipMemcpyHostToDevice);
+            if (e == hipSuccess)
+                e = hipMemcpy(h->farena + h->f_filt, t.filt.data(), 4 * t.filt.size(), hipMemcpyHostToDevice);
+            if (e != hipSuccess) rc = fail(nullptr, WENC_EHIP, "wenc_create: table upload: %s", hipGetErrorString(e));
+        }
+    }
     if (rc != WENC_OK) {
         if (h->warena) hipFree(h->warena);
         if (h->sarena) hipFree(h->sarena);
+        if (h->farena) hipFree(h->farena);
         delete h;
         return rc;
     }
@@ -656,6 +717,29 @@ int wenc_prepare_cross(wenc_t *h, const float *memory, int32_t batch, int32_t n_
     return WENC_OK;
 }
 
+int wenc_log_mel(wenc_t *h, const float *audio, int32_t batch, float *mel, void *stream) {
+    if (!h) return fail(nullptr, WENC_EINVAL, "wenc_log_mel: handle is NULL");
+    const wenc_config &c = h->cfg;
+    if (const char *m = wk::logmel_check(batch, c.n_frames, c.n_mels))
+        return fail(&h->err, WENC_EINVAL, "wenc_log_mel: %s", m);
+    if (!h->farena) return fail(&h->err, WENC_ESTATE, "wenc_log_mel: frontend tables missing");
+    if (batch == 0) return WENC_OK;
+    if (!audio || !mel) return fail(&h->err, WENC_EINVAL, "wenc_log_mel: audio and mel must be non-null");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const float *tab = reinterpret_cast<const float *>(h->farena);
+    const float *win = reinterpret_cast<const float *>(h->farena + h->f_win);
+    const float *filt = reinterpret_cast<const float *>(h->farena + h->f_filt);
+    float *blk = reinterpret_cast<float *>(h->farena + h->f_blk);
+    for (int b0 = 0; b0 < batch; b0 += c.max_batch) {
+        const int nb = batch - b0 < c.max_batch ? batch - b0 : c.max_batch;
+        WENC_TRY(h->site(WENC_SITE_MEL, st, [&] {
+            return wk::launch_logmel(audio + size_t(b0) * c.n_frames * 160, nb, c.n_frames, tab, win, filt, c.n_mels,
+                                     mel + size_t(b0) * c.n_frames * c.n_mels, blk, st);
+        }));
+    }
+    return WENC_OK;
+}
+
 void wenc_destroy(wenc_t *h) {
     if (!h) return;
     hipDeviceSynchronize();
@@ -667,6 +751,7 @@ void wenc_destroy(wenc_t *h) {
     if (h->warena) hipFree(h->warena);
     if (h->sarena) hipFree(h->sarena);
     if (h->xarena) hipFree(h->xarena);
+    if (h->farena) hipFree(h->farena);
     delete h;
 }
 

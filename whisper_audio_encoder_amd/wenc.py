@@ -26,7 +26,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 WENC_OK, WENC_EINVAL, WENC_ENOMEM, WENC_ENODEV, WENC_ESTATE, WENC_EHIP = 0, -1, -2, -3, -4, -5
 WENC_TAP_C1, WENC_TAP_STEM, WENC_TAP_BLOCK = 0, 1, 2
 WENC_EPI_GELU_F16, WENC_EPI_CONV2, WENC_EPI_RESID, WENC_EPI_QKV, WENC_EPI_KV = 0, 1, 2, 3, 4
-SITES = ("ingest", "conv1", "conv2", "ln1", "qkv", "attn", "oproj", "ln2", "fc1", "fc2", "lnf", "xcvt", "xkv")
+SITES = ("ingest", "conv1", "conv2", "ln1", "qkv", "attn", "oproj", "ln2", "fc1", "fc2", "lnf", "xcvt", "xkv", "mel")
 N_SITES = len(SITES)
 
 
@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
     L.wenc_load_cross.restype = ctypes.c_int
     L.wenc_prepare_cross.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     L.wenc_prepare_cross.restype = ctypes.c_int
+    L.wenc_log_mel.argtypes = [vp, vp, i32, vp, vp]
+    L.wenc_log_mel.restype = ctypes.c_int
     L.wenc_forward_ctx.argtypes = [vp, vp, i32, i32, vp, vp]
     L.wenc_forward_ctx.restype = ctypes.c_int
     L.wenc_forward_tap.argtypes = [vp, vp, i32, i32, vp, vp]
@@ -164,6 +166,10 @@ def wenc_forward(h, mel: torch.Tensor, batch: int, out: torch.Tensor, stream=Non
 
 def wenc_forward_ctx(h, mel: torch.Tensor, batch: int, n_ctx: int, out: torch.Tensor, stream=None) -> None:
     _check(lib().wenc_forward_ctx(h, _ptr(mel), batch, n_ctx, _ptr(out), _stream(stream)), h)
+
+
+def wenc_log_mel(h, audio: torch.Tensor, batch: int, mel: torch.Tensor, stream=None) -> None:
+    _check(lib().wenc_log_mel(h, _ptr(audio), batch, _ptr(mel), _stream(stream)), h)
 
 
 def wenc_cross_nbytes(cfg: wenc_config, n_dec_layer: int) -> int:
@@ -253,6 +259,19 @@ class Encoder:
         else:
             wenc_forward_ctx(self.h, mel, B, n_ctx, out, stream)
         return out
+
+    def log_mel(self, audio: torch.Tensor, mel: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """Log-mel of whole windows: audio [batch, 160 n_frames] fp32 ->
+        mel [batch, n_frames, n_mels] fp32, the layout forward() reads."""
+        c = self.cfg
+        if not (audio.is_cuda and audio.dtype == torch.float32 and audio.is_contiguous()
+                and audio.dim() == 2 and audio.shape[1] == 160 * c.n_frames):
+            raise ValueError(f"audio must be a contiguous fp32 device tensor [batch, {160 * c.n_frames}]")
+        B = audio.shape[0]
+        if mel is None:
+            mel = torch.empty((B, c.n_frames, c.n_mels), dtype=torch.float32, device=audio.device)
+        wenc_log_mel(self.h, audio, B, mel, stream)
+        return mel
 
     def load_cross(self, blob: np.ndarray, n_dec_layer: int) -> None:
         """Load the decoder layers' cross-attention K/V weights (x_wk, x_wv, x_bv)."""
