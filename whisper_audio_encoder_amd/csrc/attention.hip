@@ -66,7 +66,9 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, const f16 *lds, uint32_t 
         : "memory");
 }
 
-__global__ void __launch_bounds__(256)
+// At most 128 VGPRs, so four waves share each SIMD (the LDS allows five
+// workgroups per CU); measured faster than three waves with no spill.
+__global__ void __launch_bounds__(256, 4)
 attn_kernel(const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__restrict__ vt,
             f16 *__restrict__ ao, int T, int H, int ldvt) {
     // Workgroup ids are dealt round-robin over the 8 XCDs; renumber them so
@@ -128,7 +130,16 @@ attn_kernel(const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__r
         o[0][r] = 0.f;
         o[1][r] = 0.f;
     }
-    float mrow = -INFINITY, lsum = 0.f;
+    // Reference point of the softmax (base 2): probabilities are taken as
+    // exp2(s - ref).  The fp16-representable part r16 of ref enters the
+    // scores through one extra MFMA per 32-key tile, a constant A fragment
+    // (1 in dimension 64 of every key, 0 in 65..79) against a B fragment
+    // holding -r16 in dimension 64 of each query, so the subtraction costs
+    // no VALU work; rlo = ref - r16 is non-zero only when |ref| > 2048 (then
+    // the wave subtracts it explicitly).
+    float ref = 0.f, rlo = 0.f, lsum = 0.f;
+    f16x8 kone = {0, 0, 0, 0, 0, 0, 0, 0}, qref = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (hh == 0) kone[0] = (f16)1.0f;
     const int fsw = swz(l32);  // == swz(row) for every fragment row of this lane
     const int nkt = (T + KT - 1) / KT;
 
@@ -139,6 +150,7 @@ attn_kernel(const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__r
         for (int kt2 = 0; kt2 < 2; ++kt2) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kt2][r] = 0.f;
+            s[kt2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kone, qref, s[kt2], 0, 0, 0);  // -r16
             const f16 *kr = ks + (kt2 * 32 + l32) * 64;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
@@ -156,25 +168,55 @@ attn_kernel(const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__r
                 }
         }
 
+        if (__any(rlo != 0.0f)) {
+#pragma unroll
+            for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kt2][r] -= rlo;
+        }
+        // s now holds score - ref.
         float mx = s[0][0];
 #pragma unroll
         for (int kt2 = 0; kt2 < 2; ++kt2)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt2][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // Lazy rescaling: the reference point mrow only moves when the tile
-        // maximum exceeds it by more than 8 (log2 units), so the running sum
-        // and O are rescaled rarely; probabilities taken against a stale
-        // reference are at most 2^8, well inside fp16 and fp32.  The result
-        // O / l is the same for any reference point.
-        if (mx > mrow + 8.0f) {
-            const float alpha = __builtin_amdgcn_exp2f(mrow - mx);  // 0 on the first tile
-            mrow = mx;
-            lsum *= alpha;
+        // Lazy rescaling: the reference point moves (to the tile maximum,
+        // rounded to fp16) on the first tile and afterwards only when the
+        // tile maximum exceeds it by more than 8 (log2 units), so the running
+        // sum and O are rescaled rarely; probabilities taken against a stale
+        // reference are at most 2^9, well inside fp16 and fp32.  The result
+        // O / l is the same for any reference point.  Lanes l and l ^ 32 hold
+        // halves of one query's keys and must share the reference, but their
+        // maxima are exchanged only when some lane of the wave needs a move.
+        if (kt == 0 || __any(mx > 8.0f)) {
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (kt == 0 || mx > 8.0f) {
+                const float target = ref + mx;
+                float nref, nlo;
+                if (fabsf(target) <= 2048.0f) {  // fp16 rounding moves it by <= 1
+                    nref = float((f16)target);
+                    nlo = 0.0f;
+                } else {
+                    nref = target;
+                    nlo = target;
+                }
+                const float shift = nref - ref;
+                // lsum and o are still 0 on the first tile, where -shift may be
+                // large enough for exp2 to overflow: scale by 0 there.
+                const float alpha = kt == 0 ? 0.0f : __builtin_amdgcn_exp2f(-shift);
+                lsum *= alpha;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                o[0][r] *= alpha;
-                o[1][r] *= alpha;
+                for (int r = 0; r < 16; ++r) {
+                    o[0][r] *= alpha;
+                    o[1][r] *= alpha;
+                }
+#pragma unroll
+                for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[kt2][r] -= shift;
+                ref = nref;
+                rlo = nlo;
+                if (hh == 0) qref[0] = (f16)(-(nref - nlo));
             }
         }
         float ps = 0.f;
@@ -182,7 +224,7 @@ attn_kernel(const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__r
         for (int kt2 = 0; kt2 < 2; ++kt2)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(s[kt2][r] - mrow);
+                const float e = __builtin_amdgcn_exp2f(s[kt2][r]);
                 s[kt2][r] = e;
                 ps += e;
             }
