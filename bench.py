@@ -113,6 +113,34 @@ def cpu_baseline(cfg, mel, params, budget_s=30.0):
 PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix
 
 
+def time_graph(enc, mel_d, out, n_ctx, steps):
+    """The same step captured once into a hipGraph (torch.cuda.CUDAGraph on a
+    default-priority side stream) and replayed: what a caller that replays
+    the forward pays, launch overhead excluded."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        enc.forward(mel_d, out, n_ctx=n_ctx)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        enc.forward(mel_d, out, n_ctx=n_ctx)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del g
+    return {"ms_per_step": ms, "value": mel_d.shape[0] / (ms * 1e-3)}
+
+
 def time_frontend(enc, model, B, steps):
     """wenc_log_mel over B synthetic windows, timed with events on the stream."""
     import torch
@@ -244,6 +272,8 @@ def main(argv=None):
     prof = wenc.wenc_profile_read(enc.h)
     wenc.wenc_profile(enc.h, 0)
     log(f"[bench] {a.steps} steps: {ms:.3f} ms/step (wall {1e3 * wall / a.steps:.3f} ms/step)")
+    graph = time_graph(enc, mel_d, out, n_ctx, a.steps)
+    log(f"[bench] hipGraph replay: {graph['ms_per_step']:.3f} ms/step")
 
     flops = cfg.flops_per_window() * B
     tflops = flops / (ms * 1e-3) / 1e12
@@ -290,6 +320,7 @@ def main(argv=None):
                    "d_ff": cfg.d_ff, "n_layer": cfg.n_layer, "n_mels": cfg.n_mels, "parallelism": "single GPU"},
         "tflops": tflops,
         "pct_fp16_peak": 100.0 * tflops / PEAK_F16_TFLOPS,
+        "graph_replay": graph,
         "site_ms_per_step": {s: warm[s][0] / n_warm for s in wenc.SITES if warm[s][1]},
         "roofline": roof,
         "cpu_baseline": cpu,
