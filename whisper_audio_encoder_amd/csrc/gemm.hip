@@ -187,6 +187,42 @@ __device__ __forceinline__ void epi_store4(const GemmP &p, int m, int n, f32x4 v
     }
 }
 
+// Row-major epilogue stores of the LDS-staged path: 8 consecutive fp16
+// outputs (n .. n+7 of row m, n + 4 <= N) or 4 consecutive fp32 outputs.
+__device__ __forceinline__ void store_f16_run(f16 *dst, int n, int N, f16x8 o) {
+    if (n + 8 <= N) {
+        *reinterpret_cast<f16x8 *>(dst) = o;
+    } else {
+        *reinterpret_cast<f16x4 *>(dst) = f16x4{o[0], o[1], o[2], o[3]};
+    }
+}
+
+template <int EPI>
+__device__ __forceinline__ void epi_row8(const GemmP &p, int m, int n, f16x8 o) {
+    if constexpr (EPI == WENC_EPI_GELU_F16) {
+        const uint32_t bi = divu(m, p.c_div);
+        const uint32_t r = m - bi * p.c_div.d;
+        store_f16_run(static_cast<f16 *>(p.C) + int64_t(bi) * p.c_bs + int64_t(r + p.c_off) * p.ldc + n, n, p.N, o);
+    } else if constexpr (EPI == WENC_EPI_KV) {
+        if (n + 8 <= p.n_split || n >= p.n_split) {
+            const bool hi = n >= p.n_split;
+            f16 *C = (hi ? p.C2 : static_cast<f16 *>(p.C)) + int64_t(m) * p.ldc + (hi ? n - p.n_split : n);
+            store_f16_run(C, n, p.N, o);
+        } else {  // a run straddling n_split (n_split % 8 == 4)
+            *reinterpret_cast<f16x4 *>(static_cast<f16 *>(p.C) + int64_t(m) * p.ldc + n) = f16x4{o[0], o[1], o[2], o[3]};
+            if (n + 4 < p.N)
+                *reinterpret_cast<f16x4 *>(p.C2 + int64_t(m) * p.ldc) = f16x4{o[4], o[5], o[6], o[7]};
+        }
+    } else if constexpr (EPI == WENC_EPI_QKV) {  // q or k columns (V^T takes the per-element path)
+        const int slice = n / p.dmodel;
+        const int c = n - slice * p.dmodel;
+        const uint32_t bb = divu(m, p.t_div);
+        const uint32_t t = m - bb * p.t_div.d;
+        f16 *dst = slice == 0 ? p.q : p.k;
+        *reinterpret_cast<f16x8 *>(dst + ((int64_t(bb) * p.H + (c >> 6)) * p.t_div.d + t) * 64 + (c & 63)) = o;
+    }
+}
+
 // TAG only separates otherwise identical instantiations (fc1 from conv1,
 // fc2 from out_proj) so that a kernel trace names each projection.
 template <int BM, int BN, int WM, int WN, int NW, int EPI, int TAG>
@@ -355,21 +391,109 @@ gemm_kernel(const GemmP p) {
         if (kt + 1 < nk) step(kt + 1, smem1, smem0);
     }
 
-    // Epilogue, in the register layout described at the accumulators.
+    // Epilogue through LDS.  Written straight from the accumulator layout,
+    // each store would cover 32 rows x 16 bytes; instead each wave stages one
+    // 32-row block at a time in a private LDS region (the k-step buffers are
+    // free now) and reads it back row-major, so the global writes are whole
+    // 128-byte (fp16) or 256-byte (fp32) row segments.  The region is the
+    // wave's own, and LDS operations of one wave complete in order, so the
+    // only barrier is the one that retires the k-step buffers.
+    constexpr bool F32OUT = EPI == WENC_EPI_CONV2 || EPI == WENC_EPI_RESID;
+    constexpr int RS = F32OUT ? WN + 4 : WN + 8;          // row stride, elements (16 bytes of padding)
+    constexpr int REGION = 32 * RS * (F32OUT ? 4 : 2);  // bytes per wave
+    static_assert(WN == 64 && (NW / 2) * REGION <= STAGE * 2, "staging fits in one k-step buffer");
+    __syncthreads();
+    char *stg = reinterpret_cast<char *>(wave < NW / 2 ? smem0 : smem1) + (wave % (NW / 2)) * REGION;
+    bool direct = false;  // V^T columns of the QKV projection keep the per-element path
+    float sc = 1.0f;
+    if constexpr (EPI == WENC_EPI_QKV) {
+        const int slice = (n0 + wn * WN) / p.dmodel;  // a wave's 64 columns are one head of q, k or v
+        direct = slice == 2;
+        sc = slice == 0 ? p.q_scale : 1.0f;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        const int m = m0 + wm * WM + i * 32 + frow;
-        if (m >= p.M) continue;
+        const int mr = m0 + wm * WM + i * 32;
+        if (mr >= p.M) break;
+        if (direct) {
+            const int m = mr + frow;
+            if (m >= p.M) continue;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * hh;
+                    if (n < p.N) {
+                        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                        epi_store4<EPI>(p, m, n, v);
+                    }
+                }
+            continue;
+        }
+        // stage: lane holds row frow, columns 32 j + 8 g + 4 hh .. +3
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * hh;
-                if (n < p.N) {
-                    f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    epi_store4<EPI>(p, m, n, v);
+                const int cl = j * 32 + 8 * g + 4 * hh;
+                const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                if constexpr (F32OUT) {
+                    f32x4 w = v;
+                    if constexpr (EPI == WENC_EPI_CONV2) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) w[e] = gelu_erf(v[e]);
+                    }
+                    *reinterpret_cast<f32x4 *>(stg + (frow * RS + cl) * 4) = w;
+                } else {
+                    f16x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (EPI == WENC_EPI_GELU_F16)
+                            o[e] = (f16)gelu_erf(v[e]);
+                        else
+                            o[e] = (f16)(v[e] * sc);
+                    }
+                    *reinterpret_cast<f16x4 *>(stg + (frow * RS + cl) * 2) = o;
                 }
             }
+        if constexpr (F32OUT) {
+            // 16 lanes per 64-float row, 4 rows per instruction
+            const int c = lane & 15, rq = lane >> 4;
+            const int n = n0 + wn * WN + c * 4;
+            f32x4 w[8], add[8];
+#pragma unroll
+            for (int it = 0; it < 8; ++it) w[it] = *reinterpret_cast<const f32x4 *>(stg + ((it * 4 + rq) * RS + c * 4) * 4);
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int m = mr + it * 4 + rq;
+                add[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (m < p.M && n < p.N) {
+                    if constexpr (EPI == WENC_EPI_RESID) {
+                        add[it] = ld4(static_cast<const float *>(p.C) + int64_t(m) * p.ldc + n);
+                    } else {
+                        const uint32_t t = m - divu(m, p.pos_div) * p.pos_div.d;
+                        add[it] = ld4(p.pos + int64_t(t) * p.N + n);
+                    }
+                }
+            }
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int m = mr + it * 4 + rq;
+                if (m < p.M && n < p.N)
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.C) + int64_t(m) * p.ldc + n) = w[it] + add[it];
+            }
+        } else {
+            // 8 lanes per 64-half row, 8 rows per instruction
+            const int c = lane & 7, r8 = lane >> 3;
+            const int n = n0 + wn * WN + c * 8;
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int r = it * 8 + r8;
+                const f16x8 o = *reinterpret_cast<const f16x8 *>(stg + (r * RS + c * 8) * 2);
+                const int m = mr + r;
+                if (m < p.M && n < p.N) epi_row8<EPI>(p, m, n, o);
+            }
+        }
     }
 }
 
@@ -395,7 +519,7 @@ hipError_t launch_tagged(const GemmP &p, int epi, int tag, hipStream_t s) {
     return tag ? launch_cfg<BM, BN, WM, WN, NW, 1>(p, epi, s) : launch_cfg<BM, BN, WM, WN, NW, 0>(p, epi, s);
 }
 
-int g_tile_override = -1;  // WENC_GEMM_TILE: 0 = 128x128, 1 = 256x256 x 8 waves, 2 = 256x256 x 4 waves
+int g_tile_override = -1;  // WENC_GEMM_TILE: 0 = 128x128 x 4 waves, 1 = 256x256 x 8 waves
 
 }  // namespace
 
@@ -482,14 +606,13 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag) {
         g_tile_override = e ? std::atoi(e) : 99;
     }
     int cfg = g_tile_override;
-    if (cfg > 2) {
+    if (cfg > 1) {
         // 256 x 256 tiles when they fill the 256 CUs nearly twice over
         const long big = long((a.M + 255) / 256) * ((a.N + 255) / 256);
         cfg = big >= 448 ? 1 : 0;
     }
     switch (cfg) {
         case 1: return launch_tagged<256, 256, 128, 64, 8>(p, a.epilogue, tag, s);
-        case 2: return launch_tagged<256, 256, 128, 128, 4>(p, a.epilogue, tag, s);
         default: return launch_tagged<128, 128, 64, 64, 4>(p, a.epilogue, tag, s);
     }
 }
