@@ -219,26 +219,25 @@ attn_kernel(const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__r
                 if (hh == 0) qref[0] = (f16)(-(nref - nlo));
             }
         }
-        float ps = 0.f;
 #pragma unroll
         for (int kt2 = 0; kt2 < 2; ++kt2)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(s[kt2][r]);
-                s[kt2][r] = e;
-                ps += e;
-            }
-        lsum += ps;
+            for (int r = 0; r < 16; ++r) s[kt2][r] = __builtin_amdgcn_exp2f(s[kt2][r]);
 
         // O^T[dim][query] += V^T[dim][slots] P^T[slots][query], 16 keys per
         // MFMA: LDS chunk 2 s4 + hh of a V^T row holds exactly the 8 keys lane
-        // half hh has probabilities for.
+        // half hh has probabilities for.  The row sum adds the same fp16
+        // probabilities the MFMA consumes, two per instruction (dot with 1, 1,
+        // accumulated in fp32).
+        const f16x2 ones = {(f16)1.0f, (f16)1.0f};
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
             const int kt2 = s4 >> 1, sg = s4 & 1;
             f16x8 pb;
 #pragma unroll
             for (int i = 0; i < 8; ++i) pb[i] = (f16)s[kt2][8 * sg + i];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lsum = __builtin_amdgcn_fdot2(f16x2{pb[2 * i], pb[2 * i + 1]}, ones, lsum, false);
 #pragma unroll
             for (int ht = 0; ht < 2; ++ht) {
                 const int dim = ht * 32 + l32;
