@@ -55,6 +55,8 @@ struct GemmP {
     f16 *q, *k, *vt;
     f16 *C2;
     int n_split;
+    int a_valid;  // rows r of a batch item with r % a_rows_per_batch >= a_valid read as zero
+    int T;        // QKV: keys per batch item (the row space is padded to t_div.d = T rounded up to 16)
     DivU t_div;
     int H, ldvt, dmodel;
     float q_scale;
@@ -129,64 +131,6 @@ __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<
 
 __device__ __forceinline__ uint32_t vt_slot(uint32_t t) { return (t & ~12u) | ((t & 4u) << 1) | ((t & 8u) >> 1); }
 
-// Store 4 consecutive output columns n .. n+3 of row m.
-template <int EPI>
-__device__ __forceinline__ void epi_store4(const GemmP &p, int m, int n, f32x4 v) {
-    if constexpr (EPI == WENC_EPI_GELU_F16) {
-        const uint32_t bi = divu(m, p.c_div);
-        const uint32_t r = m - bi * p.c_div.d;
-        f16 *C = static_cast<f16 *>(p.C) + int64_t(bi) * p.c_bs + int64_t(r + p.c_off) * p.ldc + n;
-        f16x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (f16)gelu_erf(v[e]);
-        *reinterpret_cast<f16x4 *>(C) = o;
-    } else if constexpr (EPI == WENC_EPI_CONV2) {
-        const uint32_t t = m - divu(m, p.pos_div) * p.pos_div.d;
-        const f32x4 ps = ld4(p.pos + int64_t(t) * p.N + n);
-        f32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = gelu_erf(v[e]) + ps[e];
-        *reinterpret_cast<f32x4 *>(static_cast<float *>(p.C) + int64_t(m) * p.ldc + n) = o;
-    } else if constexpr (EPI == WENC_EPI_RESID) {
-        f32x4 *C = reinterpret_cast<f32x4 *>(static_cast<float *>(p.C) + int64_t(m) * p.ldc + n);
-        *C = *C + v;
-    } else if constexpr (EPI == WENC_EPI_KV) {
-        const bool hi = n >= p.n_split;  // a run of 4 never straddles n_split (both multiples of 4)
-        f16 *C = (hi ? p.C2 : static_cast<f16 *>(p.C)) + int64_t(m) * p.ldc + (hi ? n - p.n_split : n);
-        f16x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (f16)v[e];
-        *reinterpret_cast<f16x4 *>(C) = o;
-    } else if constexpr (EPI == WENC_EPI_QKV) {
-        const int slice = n / p.dmodel;
-        const int c = n - slice * p.dmodel;
-        const int h = c >> 6, e = c & 63;
-        const uint32_t bb = divu(m, p.t_div);
-        const uint32_t t = m - bb * p.t_div.d;
-        const int64_t bh = int64_t(bb) * p.H + h;
-        if (slice < 2) {
-            const float sc = slice == 0 ? p.q_scale : 1.0f;
-            f16x4 o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = (f16)(v[i] * sc);
-            f16 *dst = slice == 0 ? p.q : p.k;
-            *reinterpret_cast<f16x4 *>(dst + (bh * p.t_div.d + t) * 64 + e) = o;
-        } else {
-            // V^T key slot: bits 2 and 3 of the key swapped, the order in which
-            // the attention kernel's lanes hold their probabilities.
-            f16 *row = p.vt + (bh * 64 + e) * p.ldvt;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) row[int64_t(i) * p.ldvt + vt_slot(t)] = (f16)v[i];
-            if (t + 1 == p.t_div.d) {
-                // the last key also clears the slots of keys T .. ldvt-1
-                for (uint32_t u = t + 1; u < uint32_t(p.ldvt); ++u)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) row[int64_t(i) * p.ldvt + vt_slot(u)] = (f16)0.0f;
-            }
-        }
-    }
-}
-
 // Row-major epilogue stores of the LDS-staged path: 8 consecutive fp16
 // outputs (n .. n+7 of row m, n + 4 <= N) or 4 consecutive fp32 outputs.
 __device__ __forceinline__ void store_f16_run(f16 *dst, int n, int N, f16x8 o) {
@@ -213,13 +157,14 @@ __device__ __forceinline__ void epi_row8(const GemmP &p, int m, int n, f16x8 o) 
             if (n + 4 < p.N)
                 *reinterpret_cast<f16x4 *>(p.C2 + int64_t(m) * p.ldc) = f16x4{o[4], o[5], o[6], o[7]};
         }
-    } else if constexpr (EPI == WENC_EPI_QKV) {  // q or k columns (V^T takes the per-element path)
+    } else if constexpr (EPI == WENC_EPI_QKV) {  // q or k columns; pad rows (t >= T) are not stored
         const int slice = n / p.dmodel;
         const int c = n - slice * p.dmodel;
         const uint32_t bb = divu(m, p.t_div);
         const uint32_t t = m - bb * p.t_div.d;
+        if (t >= uint32_t(p.T)) return;
         f16 *dst = slice == 0 ? p.q : p.k;
-        *reinterpret_cast<f16x8 *>(dst + ((int64_t(bb) * p.H + (c >> 6)) * p.t_div.d + t) * 64 + (c & 63)) = o;
+        *reinterpret_cast<f16x8 *>(dst + ((int64_t(bb) * p.H + (c >> 6)) * p.T + t) * 64 + (c & 63)) = o;
     }
 }
 
@@ -253,7 +198,10 @@ gemm_kernel(const GemmP p) {
     // Direct loads: one instruction moves 8 tile rows x 128 B; lane i lands at
     // row r = 8 g + (i >> 3), chunk position i & 7, so it fetches logical
     // chunk (i & 7) ^ sw(r).
-    const int64_t a0 = a_row(p, m0);
+    // Tile base: the row of m0, or for a pad row (QKV) the start of the next
+    // batch item, so that every row offset below is non-negative.
+    const uint32_t b0 = divu(m0, p.a_div);
+    const int64_t a0 = int64_t(b0) * p.a_bs + int64_t(min(int(m0 - b0 * p.a_div.d), p.a_valid)) * p.lda;
     const int lw = wave < LW ? wave : 0;  // offsets of the waves that load
     uint32_t a_off[AG], a_ch[AG];
 #pragma unroll
@@ -261,7 +209,8 @@ gemm_kernel(const GemmP p) {
         const int r = (lw * AG + g) * 8 + (lane >> 3);
         a_ch[g] = (lane & 7) ^ swz(r);
         const int m = m0 + r;
-        a_off[g] = m < p.M ? uint32_t((a_row(p, m) - a0) * 2) + a_ch[g] * 16 : OOB;
+        const bool ok = m < p.M && int(m - divu(m, p.a_div) * p.a_div.d) < p.a_valid;
+        a_off[g] = ok ? uint32_t((a_row(p, m) - a0) * 2) + a_ch[g] * 16 : OOB;
     }
     uint32_t b_off[BG], b_ch[BG];
 #pragma unroll
@@ -404,32 +353,19 @@ gemm_kernel(const GemmP p) {
     static_assert(WN == 64 && (NW / 2) * REGION <= STAGE * 2, "staging fits in one k-step buffer");
     __syncthreads();
     char *stg = reinterpret_cast<char *>(wave < NW / 2 ? smem0 : smem1) + (wave % (NW / 2)) * REGION;
-    bool direct = false;  // V^T columns of the QKV projection keep the per-element path
+    bool vtile = false;  // QKV: this wave's 64 columns are one head of v
+    int vhead = 0;
     float sc = 1.0f;
     if constexpr (EPI == WENC_EPI_QKV) {
         const int slice = (n0 + wn * WN) / p.dmodel;  // a wave's 64 columns are one head of q, k or v
-        direct = slice == 2;
+        vtile = slice == 2;
+        vhead = ((n0 + wn * WN) - 2 * p.dmodel) >> 6;
         sc = slice == 0 ? p.q_scale : 1.0f;
     }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int mr = m0 + wm * WM + i * 32;
         if (mr >= p.M) break;
-        if (direct) {
-            const int m = mr + frow;
-            if (m >= p.M) continue;
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * hh;
-                    if (n < p.N) {
-                        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                        epi_store4<EPI>(p, m, n, v);
-                    }
-                }
-            continue;
-        }
         // stage: lane holds row frow, columns 32 j + 8 g + 4 hh .. +3
 #pragma unroll
         for (int j = 0; j < TN; ++j)
@@ -481,6 +417,49 @@ gemm_kernel(const GemmP p) {
                 const int m = mr + it * 4 + rq;
                 if (m < p.M && n < p.N)
                     *reinterpret_cast<f32x4 *>(static_cast<float *>(p.C) + int64_t(m) * p.ldc + n) = w[it] + add[it];
+            }
+        } else if (vtile) {
+            if constexpr (EPI == WENC_EPI_QKV) {
+                // V^T [b][h][dim][slot]: the block's 32 rows are two 16-key
+                // groups of one batch item each (the row space is padded to a
+                // multiple of 16 keys).  A run is 8 consecutive slots of one
+                // dimension: slots 16 G + 8 s8 .. +7 hold keys 16 G +
+                // vt_slot(8 s8 + q) (the slot order is an involution).  Four
+                // consecutive lanes cover one dimension's 32 slots; keys at or
+                // past T are written as zeros.
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int run = it * 64 + lane;
+                    const int s8 = run & 1, gr = (run >> 1) & 1, e = run >> 2;
+                    const uint32_t mg = uint32_t(mr + 16 * gr);
+                    const uint32_t bb = divu(mg, p.t_div);
+                    const uint32_t t0 = mg - bb * p.t_div.d;
+                    f16x8 o;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const uint32_t key = vt_slot(uint32_t(8 * s8 + q));
+                        const f16 val = *reinterpret_cast<const f16 *>(stg + ((16 * gr + key) * RS + e) * 2);
+                        o[q] = t0 + key < uint32_t(p.T) ? val : (f16)0.0f;
+                    }
+                    if (int(mg) < p.M)
+                        *reinterpret_cast<f16x8 *>(p.vt + ((int64_t(bb) * p.H + vhead) * 64 + e) * p.ldvt + t0 + 8 * s8) = o;
+                }
+                // the last key group of a batch item also clears slots
+                // t_div.d .. ldvt-1 of its 64 dimensions
+#pragma unroll
+                for (int gr = 0; gr < 2; ++gr) {
+                    const uint32_t mg = uint32_t(mr + 16 * gr);
+                    const uint32_t bb = divu(mg, p.t_div);
+                    const uint32_t t0 = mg - bb * p.t_div.d;
+                    if (int(mg) < p.M && t0 + 16 == p.t_div.d) {
+                        const int nz = (p.ldvt - int(p.t_div.d)) / 8;
+                        for (int run = lane; run < nz * 64; run += 64) {
+                            const int e = run & 63, zc = run >> 6;
+                            *reinterpret_cast<f16x8 *>(p.vt + ((int64_t(bb) * p.H + vhead) * 64 + e) * p.ldvt +
+                                                       p.t_div.d + 8 * zc) = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                        }
+                    }
+                }
             }
         } else {
             // 8 lanes per 64-half row, 8 rows per instruction
@@ -558,6 +537,9 @@ const char *gemm_check(const wenc_gemm_args &a) {
             if (a.n_head <= 0 || a.N != 3 * 64 * a.n_head) return "gemm: QKV needs N == 3 * 64 * n_head";
             if (a.T <= 0 || a.T >= (1 << 16) || a.M % a.T) return "gemm: QKV needs 0 < T < 65536 and M % T == 0";
             if (a.ldvt < a.T || a.ldvt % 64) return "gemm: ldvt must be a multiple of 64 and >= T";
+            if (!(a.a_rows_per_batch >= a.M || a.a_batch_stride == int64_t(a.a_rows_per_batch) * a.lda))
+                return "gemm: QKV needs row-linear A (row m at m * lda)";
+            if (int64_t(a.M / a.T) * ((a.T + 15) & ~15) >= (1 << 24)) return "gemm: QKV rows padded to 16 keys must be < 2^24";
             break;
         case WENC_EPI_KV:
             if (!a.C) return "gemm: C is null";
@@ -601,6 +583,19 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag) {
     p.M = a.M;
     p.N = a.N;
     p.K = a.K;
+    p.a_valid = 1 << 30;
+    p.T = a.T;
+    if (a.epilogue == WENC_EPI_QKV) {
+        // Rows are padded to a multiple of 16 keys per batch item, so that a
+        // 16-row block of the tile is one V^T slot group; pad rows read zero
+        // (row-linear A, checked by gemm_check) and are not stored.
+        const int tp = (a.T + 15) & ~15;
+        p.M = (a.M / a.T) * tp;
+        p.a_div = make_divu(tp);
+        p.a_bs = int64_t(a.T) * a.lda;
+        p.a_valid = a.T;
+        p.t_div = make_divu(tp);
+    }
     if (g_tile_override < 0) {
         const char *e = std::getenv("WENC_GEMM_TILE");
         g_tile_override = e ? std::atoi(e) : 99;
@@ -608,7 +603,7 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag) {
     int cfg = g_tile_override;
     if (cfg > 1) {
         // 256 x 256 tiles when they fill the 256 CUs nearly twice over
-        const long big = long((a.M + 255) / 256) * ((a.N + 255) / 256);
+        const long big = long((p.M + 255) / 256) * ((a.N + 255) / 256);
         cfg = big >= 448 ? 1 : 0;
     }
     switch (cfg) {
