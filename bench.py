@@ -113,6 +113,29 @@ def cpu_baseline(cfg, mel, params, budget_s=30.0):
 PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix
 
 
+def device_peak():
+    """Dense fp16 MFMA peak from the device's own properties: CUs x 4096
+    FLOP per clock (4 SIMDs x 1024) x the maximum engine clock."""
+    import ctypes
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    cus = pr.multi_processor_count
+    clk = 0
+    try:  # hipDeviceGetAttribute(&v, hipDeviceAttributeClockRate (5), device 0): peak clock in kHz
+        hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0:
+            clk = v.value
+    except OSError:
+        pass
+    out = {"name": pr.name, "gcn_arch": getattr(pr, "gcnArchName", ""), "compute_units": cus,
+           "assumed_peak_tflops": PEAK_F16_TFLOPS}
+    if clk:
+        out["max_clock_mhz"] = clk / 1e3
+        out["peak_from_clock_tflops"] = cus * 4096 * clk * 1e3 / 1e12
+    return out
+
+
 def time_graph(enc, mel_d, out, n_ctx, steps):
     """The same step captured once into a hipGraph (torch.cuda.CUDAGraph on a
     default-priority side stream) and replayed: what a caller that replays
@@ -272,6 +295,16 @@ def main(argv=None):
     prof = wenc.wenc_profile_read(enc.h)
     wenc.wenc_profile(enc.h, 0)
     log(f"[bench] {a.steps} steps: {ms:.3f} ms/step (wall {1e3 * wall / a.steps:.3f} ms/step)")
+    # per-call times (median, minimum) from events around each forward
+    per_call = []
+    for _ in range(max(a.steps // 2, 3)):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        enc.forward(mel_d, out, n_ctx=n_ctx)
+        c1.record(stream)
+        per_call.append((c0, c1))
+    torch.cuda.synchronize()
+    call_ms = sorted(c0.elapsed_time(c1) for c0, c1 in per_call)
     graph = time_graph(enc, mel_d, out, n_ctx, a.steps)
     log(f"[bench] hipGraph replay: {graph['ms_per_step']:.3f} ms/step")
 
@@ -320,7 +353,9 @@ def main(argv=None):
                    "d_ff": cfg.d_ff, "n_layer": cfg.n_layer, "n_mels": cfg.n_mels, "parallelism": "single GPU"},
         "tflops": tflops,
         "pct_fp16_peak": 100.0 * tflops / PEAK_F16_TFLOPS,
+        "per_call_ms": {"median": call_ms[len(call_ms) // 2], "min": call_ms[0], "calls": len(call_ms)},
         "graph_replay": graph,
+        "device_peak": device_peak(),
         "site_ms_per_step": {s: warm[s][0] / n_warm for s in wenc.SITES if warm[s][1]},
         "roofline": roof,
         "cpu_baseline": cpu,
