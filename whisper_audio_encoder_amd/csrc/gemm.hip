@@ -99,25 +99,30 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base) {
 }
 
 // One 16-byte-per-lane global -> LDS transfer of 1 KB: lane i's data lands
-// at lds + 16 i.  Written as inline assembly so that the compiler does not
-// see an LDS store: it would otherwise wait for every such transfer before
-// later LDS reads of the other buffer.  The main loop orders the transfers
-// itself (s_waitcnt vmcnt(0) + barrier before any wave reads the buffer
-// they fill).  M0 carries the LDS address; nothing else in these kernels
-// uses M0.  The descriptor words go through readfirstlane so that the
-// operand stays in scalar registers inside branches on the wave index.
-__device__ __forceinline__ void load_lds16(i32x4 rsrc, const f16 *lds, uint32_t voffset) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) f16 *)lds)));
+// at LDS byte address lds + 16 i.  Written as inline assembly so that the
+// compiler does not see an LDS store: it would otherwise wait for every such
+// transfer before later LDS reads of the other buffer.  The main loop orders
+// the transfers itself (s_waitcnt vmcnt(0) + barrier before any wave reads
+// the buffer they fill).  M0 carries the LDS address; nothing else in these
+// kernels uses M0.  The descriptor words go through readfirstlane so that
+// the operand stays in scalar registers inside branches on the wave index.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds, uint32_t voffset) {
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
         "buffer_load_dwordx4 %1, %2, 0 offen lds"
         :
-        : "s"(m0), "v"(voffset),
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset),
           "s"(i32x4{__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
                     __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])})
         : "memory");
+}
+
+// LDS byte address of a __shared__ object (the generic-to-LDS cast carries a
+// null check, so it is taken once per kernel).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane(
+        uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char *)p)));
 }
 
 // LDS chunk swizzle.  A tile row is 128 B (8 chunks of 16 B); logical chunk c
@@ -170,12 +175,16 @@ __device__ __forceinline__ void epi_row8(const GemmP &p, int m, int n, f16x8 o) 
 
 // TAG only separates otherwise identical instantiations (fc1 from conv1,
 // fc2 from out_proj) so that a kernel trace names each projection.
+// A 256 x 256 tile runs one workgroup per CU (its LDS allows one); the
+// 128 x 128 kernel is held to two workgroups per CU (its LDS allows two).
+// (A 4-wave 256 x 256 kernel with 128 x 128 per wave, accumulators in
+// AGPRs, compiles from this template too; it measured 10-20% slower.)
 template <int BM, int BN, int WM, int WN, int NW, int EPI, int TAG>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __launch_bounds__(NW * 64, (NW >= 8 || BM >= 256) ? 1 : 2)
 gemm_kernel(const GemmP p) {
     constexpr int WAVES_N = BN / WN;
     static_assert((BM / WM) * (BN / WN) == NW, "wave grid");
-    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int TM = WM / 16, TN = WN / 16;
     // Waves that issue the direct loads.  With 8 waves two share each SIMD
     // (wave w runs on SIMD w % 4); only waves 0..3 load, so their partners
     // issue MFMAs without queueing behind vector-memory instructions
@@ -222,255 +231,264 @@ gemm_kernel(const GemmP p) {
     const i32x4 ra = make_rsrc(p.A + a0);
     const i32x4 rb = make_rsrc(p.W + int64_t(n0) * p.ldw);
 
-    auto issue = [&](int kt, f16 *st) {
+    const uint32_t lds0 = lds_addr(smem0), lds1 = lds_addr(smem1);
+    // Direct loads of K step kt into the stage at LDS byte address st.  Steps
+    // that lie wholly inside K (every step when K % 64 == 0) skip the K-tail
+    // test.
+    auto issue = [&](int kt, uint32_t st) __attribute__((always_inline)) {
         if (wave >= LW) return;
         const uint32_t kb = uint32_t(kt) * (BK * 2);
+        if ((kt + 1) * BK <= p.K) {
 #pragma unroll
-        for (int g = 0; g < AG; ++g) {
-            const uint32_t kflag = (kt * BK + int(a_ch[g]) * 8 < p.K) ? 0u : OOB;
-            load_lds16(ra, st + (lw * AG + g) * 8 * BK, (a_off[g] | kflag) + kb);
-        }
+            for (int g = 0; g < AG; ++g) load_lds16(ra, st + (lw * AG + g) * 8 * BK * 2, a_off[g] + kb);
 #pragma unroll
-        for (int g = 0; g < BG; ++g) {
-            const uint32_t kflag = (kt * BK + int(b_ch[g]) * 8 < p.K) ? 0u : OOB;
-            load_lds16(rb, st + BM * BK + (lw * BG + g) * 8 * BK, (b_off[g] | kflag) + kb);
+            for (int g = 0; g < BG; ++g) load_lds16(rb, st + (BM + (lw * BG + g) * 8) * BK * 2, b_off[g] + kb);
+        } else {
+#pragma unroll
+            for (int g = 0; g < AG; ++g) {
+                const uint32_t kflag = (kt * BK + int(a_ch[g]) * 8 < p.K) ? 0u : OOB;
+                load_lds16(ra, st + (lw * AG + g) * 8 * BK * 2, (a_off[g] | kflag) + kb);
+            }
+#pragma unroll
+            for (int g = 0; g < BG; ++g) {
+                const uint32_t kflag = (kt * BK + int(b_ch[g]) * 8 < p.K) ? 0u : OOB;
+                load_lds16(rb, st + (BM + (lw * BG + g) * 8) * BK * 2, (b_off[g] | kflag) + kb);
+            }
         }
     };
 
-    // Register r of accumulator tile (i, j) holds row (lane & 31) of the i-th
-    // 32-row block and column 8 (r >> 2) + 4 (lane >> 5) + (r & 3) of the j-th
-    // 32-column block.  Every accumulator starts at its column's bias, so the
-    // epilogues add none.
-    const int hh = lane >> 5;
-    f32x16 acc[TM][TN];
+    // Accumulator (i, j) is the 16 x 16 block of rows 16 i and columns 16 j of
+    // the wave's tile; its register r holds row (lane & 15) and column
+    // 4 (lane >> 4) + r.  Every accumulator starts at its column's bias, so
+    // the epilogues add none.
+    const int hh = lane >> 4;
+    f32x4 acc[TM][TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * WN + j * 16 + 4 * hh;
+        const f32x4 b = n < p.N ? ld4(p.bias + n) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * hh;
-            const f32x4 b = n < p.N ? ld4(p.bias + n) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] = b[e];
-        }
+        for (int i = 0; i < TM; ++i) acc[i][j] = b;
+    }
 
-    // Fragment reads: lane supplies row (lane & 31) of a 32-row tile and k
-    // values 8 (lane >> 5) .. +7 of the current 16-wide slice.  Two fragment
-    // sets alternate so the reads of slice kk+1 are in flight during the
-    // MFMAs of slice kk; sched_barrier keeps the compiler from hoisting every
-    // read of the step up front (which would need 4 sets of registers).
-    const int frow = lane & 31;
-    const int fsw = swz(lane & 31);  // == swz(row) for every fragment row of this lane
-    auto load_frags = [&](const f16 *st, int kk, f16x8 (&af)[TM], f16x8 (&bf)[TN]) {
-        const f16 *as = st + (wm * WM + frow) * BK;
-        const f16 *bs = st + BM * BK + (wn * WN + frow) * BK;
-        const int ch = ((kk * 2 + (lane >> 5)) ^ fsw) << 3;
-        // read in the order the MFMAs below consume them: b0, a0 .. a(TM-1), b1 ..
-        bf[0] = *reinterpret_cast<const f16x8 *>(bs + ch);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const f16x8 *>(as + i * 32 * BK + ch);
-#pragma unroll
-        for (int j = 1; j < TN; ++j) bf[j] = *reinterpret_cast<const f16x8 *>(bs + j * 32 * BK + ch);
-    };
-    auto mfmas = [&](const f16x8 (&af)[TM], const f16x8 (&bf)[TN]) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
-    };
-    // Interleave the next slice's fragment reads with this slice's MFMAs:
-    // one LDS read, then MFMAs, repeated, so every read has several MFMAs
-    // (32 cycles each) to land before its consumer.
-    auto interleave = [&]() {
-        constexpr int NR = TM + TN, NM = TM * TN;
-        constexpr int PER = NM / NR > 0 ? NM / NR : 1;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
-            __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMA
-        }
-        if constexpr (NM > NR * PER) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR * PER, 0);
-    };
-    static_assert(BK == 64, "the main loop walks four 16-wide k slices per step");
+    // Fragment reads (v_mfma_f32_16x16x32_f16 operands): lane supplies row
+    // (lane & 15) of a 16-row block and k values 8 (lane >> 4) .. +7 of the
+    // current 32-wide slice, one 16-byte LDS read per block.
+    const int frow = lane & 15;
+    const int fsw = swz(lane & 15);  // == swz(row) for every fragment row of this lane
+    static_assert(BK == 64, "the main loop walks two 32-wide k slices per step");
 
-    // Main loop.  Slice kk of step kt is read into fragment set (kk & 1)
-    // while the MFMAs of slice kk-1 run.  The barrier that publishes step
-    // kt+1 sits before the MFMAs of the last slice of step kt (whose
-    // fragments are already in registers), so those MFMAs overlap both the
-    // barrier and the first fragment reads of step kt+1, and the direct
-    // loads of step kt+2 go into the buffer step kt has just released.
-    // Steps alternate between the two LDS buffers in a loop unrolled by
-    // two, so every LDS access names its buffer statically and the compiler
-    // can tell a transfer into one buffer from reads of the other.
+    // Main loop.  A step of 64 k is two slices of 32.  Fragments roll: the
+    // A-side fragment of block row i for the next slice is read as soon as
+    // the MFMAs of block row i of this slice are issued, into the same
+    // registers, and the W-side fragments alternate between two sets; so
+    // every read has most of a slice of MFMAs to land before its consumer,
+    // with one A-side set live.  The barrier that publishes step kt+1 sits
+    // between the two slices of step kt: slice 1's fragments are already in
+    // registers, so its MFMAs overlap the barrier and the reads of step
+    // kt+1's slice 0, and the direct loads of step kt+2 go into the buffer
+    // step kt has just released.  Steps alternate between the two LDS
+    // buffers in a loop unrolled by two, so every LDS access names its buffer
+    // statically and the compiler can tell a transfer into one buffer from
+    // reads of the other.  (The last step's slice 1 reads the idle buffer;
+    // those fragments are not used.)
     const int nk = (p.K + BK - 1) / BK;
-    f16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-    auto step = [&](int kt, f16 *cur, f16 *nxt) {
-        load_frags(cur, 1, fa1, fb1);
-        mfmas(fa0, fb0);
-        interleave();
-        __builtin_amdgcn_sched_barrier(0);
-        load_frags(cur, 2, fa0, fb0);
-        mfmas(fa1, fb1);
-        interleave();
-        __builtin_amdgcn_sched_barrier(0);
-        load_frags(cur, 3, fa1, fb1);
-        mfmas(fa0, fb0);
-        interleave();
-        __builtin_amdgcn_sched_barrier(0);
-        if (kt + 1 < nk) {
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-            __syncthreads();
-            if (kt + 2 < nk) issue(kt + 2, cur);
-            load_frags(nxt, 0, fa0, fb0);
+    f16x8 af[TM], bf0[TN], bf1[TN];
+    auto slice = [&](const f16x8 (&bfc)[TN], f16x8 (&bfn)[TN], const f16 *src, int kk) __attribute__((always_inline)) {
+        const f16 *as = src + (wm * WM + frow) * BK;
+        const f16 *bs = src + BM * BK + (wn * WN + frow) * BK;
+        const int ch = ((kk * 4 + (lane >> 4)) ^ fsw) << 3;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bfc[j], af[i], acc[i][j], 0, 0, 0);
+            if (i < TN) bfn[i] = *reinterpret_cast<const f16x8 *>(bs + i * 16 * BK + ch);
+            af[i] = *reinterpret_cast<const f16x8 *>(as + i * 16 * BK + ch);
         }
-        mfmas(fa1, fb1);
-        interleave();
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+#pragma unroll
+        for (int i = TN; i < TM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+    auto step = [&](int kt, f16 *cur, f16 *nxt, uint32_t cur_lds) __attribute__((always_inline)) {
+        slice(bf0, bf1, cur, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (kt + 2 < nk) issue(kt + 2, cur_lds);
+        __builtin_amdgcn_sched_barrier(0);
+        slice(bf1, bf0, nxt, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
-    issue(0, smem0);
+    issue(0, lds0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (nk > 1) issue(1, smem1);
-    load_frags(smem0, 0, fa0, fb0);
+    if (nk > 1) issue(1, lds1);
+    {
+        const f16 *as = smem0 + (wm * WM + frow) * BK;
+        const f16 *bs = smem0 + BM * BK + (wn * WN + frow) * BK;
+        const int ch = ((lane >> 4) ^ fsw) << 3;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const f16x8 *>(as + i * 16 * BK + ch);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bf0[j] = *reinterpret_cast<const f16x8 *>(bs + j * 16 * BK + ch);
+    }
 #pragma unroll 1
     for (int kt = 0; kt < nk; kt += 2) {
-        step(kt, smem0, smem1);
-        if (kt + 1 < nk) step(kt + 1, smem1, smem0);
+        step(kt, smem0, smem1, lds0);
+        if (kt + 1 < nk) step(kt + 1, smem1, smem0, lds1);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue through LDS.  Written straight from the accumulator layout,
-    // each store would cover 32 rows x 16 bytes; instead each wave stages one
-    // 32-row block at a time in a private LDS region (the k-step buffers are
-    // free now) and reads it back row-major, so the global writes are whole
-    // 128-byte (fp16) or 256-byte (fp32) row segments.  The region is the
-    // wave's own, and LDS operations of one wave complete in order, so the
-    // only barrier is the one that retires the k-step buffers.
+    // each store would cover 16 rows x 16 bytes; instead each wave stages one
+    // 32-row x 64-column block at a time in a private LDS region (the k-step
+    // buffers are free now) and reads it back row-major, so the global
+    // writes are whole 128-byte (fp16) or 256-byte (fp32) row segments.  The
+    // region is the wave's own, and LDS operations of one wave complete in
+    // order, so the only barrier is the one that retires the k-step buffers.
     constexpr bool F32OUT = EPI == WENC_EPI_CONV2 || EPI == WENC_EPI_RESID;
-    constexpr int RS = F32OUT ? WN + 4 : WN + 8;          // row stride, elements (16 bytes of padding)
+    constexpr int RS = F32OUT ? 64 + 4 : 64 + 8;        // row stride, elements (16 bytes of padding)
     constexpr int REGION = 32 * RS * (F32OUT ? 4 : 2);  // bytes per wave
-    static_assert(WN == 64 && (NW / 2) * REGION <= STAGE * 2, "staging fits in one k-step buffer");
+    static_assert(WN % 64 == 0 && WM % 32 == 0 && (NW / 2) * REGION <= STAGE * 2, "staging fits in one k-step buffer");
     __syncthreads();
     char *stg = reinterpret_cast<char *>(wave < NW / 2 ? smem0 : smem1) + (wave % (NW / 2)) * REGION;
-    bool vtile = false;  // QKV: this wave's 64 columns are one head of v
-    int vhead = 0;
-    float sc = 1.0f;
-    if constexpr (EPI == WENC_EPI_QKV) {
-        const int slice = (n0 + wn * WN) / p.dmodel;  // a wave's 64 columns are one head of q, k or v
-        vtile = slice == 2;
-        vhead = ((n0 + wn * WN) - 2 * p.dmodel) >> 6;
-        sc = slice == 0 ? p.q_scale : 1.0f;
-    }
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int mr = m0 + wm * WM + i * 32;
-        if (mr >= p.M) break;
-        // stage: lane holds row frow, columns 32 j + 8 g + 4 hh .. +3
+    for (int cg = 0; cg < WN / 64; ++cg) {
+        const int nw = n0 + wn * WN + cg * 64;  // first column of this 64-column group
+        bool vtile = false;                     // QKV: the group is one head of v
+        int vhead = 0;
+        float sc = 1.0f;
+        if constexpr (EPI == WENC_EPI_QKV) {
+            const int slice = nw / p.dmodel;  // a 64-column group is one head of q, k or v
+            vtile = slice == 2;
+            vhead = (nw - 2 * p.dmodel) >> 6;
+            sc = slice == 0 ? p.q_scale : 1.0f;
+        }
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int i2 = 0; i2 < WM / 32; ++i2) {
+            const int mr = m0 + wm * WM + i2 * 32;
+            if (mr >= p.M) break;
+            // stage: lane holds row 16 g + frow, columns 16 j + 4 hh .. +3
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int cl = j * 32 + 8 * g + 4 * hh;
-                const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                if constexpr (F32OUT) {
-                    f32x4 w = v;
-                    if constexpr (EPI == WENC_EPI_CONV2) {
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) w[e] = gelu_erf(v[e]);
-                    }
-                    *reinterpret_cast<f32x4 *>(stg + (frow * RS + cl) * 4) = w;
-                } else {
-                    f16x4 o;
+                for (int g = 0; g < 2; ++g) {
+                    const int cl = j * 16 + 4 * hh;
+                    const int srow = 16 * g + frow;
+                    const f32x4 v = acc[2 * i2 + g][cg * 4 + j];
+                    if constexpr (F32OUT) {
+                        f32x4 w = v;
+                        if constexpr (EPI == WENC_EPI_CONV2) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if constexpr (EPI == WENC_EPI_GELU_F16)
-                            o[e] = (f16)gelu_erf(v[e]);
-                        else
-                            o[e] = (f16)(v[e] * sc);
-                    }
-                    *reinterpret_cast<f16x4 *>(stg + (frow * RS + cl) * 2) = o;
-                }
-            }
-        if constexpr (F32OUT) {
-            // 16 lanes per 64-float row, 4 rows per instruction
-            const int c = lane & 15, rq = lane >> 4;
-            const int n = n0 + wn * WN + c * 4;
-            f32x4 w[8], add[8];
-#pragma unroll
-            for (int it = 0; it < 8; ++it) w[it] = *reinterpret_cast<const f32x4 *>(stg + ((it * 4 + rq) * RS + c * 4) * 4);
-#pragma unroll
-            for (int it = 0; it < 8; ++it) {
-                const int m = mr + it * 4 + rq;
-                add[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (m < p.M && n < p.N) {
-                    if constexpr (EPI == WENC_EPI_RESID) {
-                        add[it] = ld4(static_cast<const float *>(p.C) + int64_t(m) * p.ldc + n);
+                            for (int e = 0; e < 4; ++e) w[e] = gelu_erf(v[e]);
+                        }
+                        *reinterpret_cast<f32x4 *>(stg + (srow * RS + cl) * 4) = w;
                     } else {
-                        const uint32_t t = m - divu(m, p.pos_div) * p.pos_div.d;
-                        add[it] = ld4(p.pos + int64_t(t) * p.N + n);
+                        f16x4 o;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if constexpr (EPI == WENC_EPI_GELU_F16)
+                                o[e] = (f16)gelu_erf(v[e]);
+                            else
+                                o[e] = (f16)(v[e] * sc);
+                        }
+                        *reinterpret_cast<f16x4 *>(stg + (srow * RS + cl) * 2) = o;
                     }
                 }
-            }
+            if constexpr (F32OUT) {
+                // 16 lanes per 64-float row, 4 rows per instruction, in two
+                // halves of 4 instructions whose residual (or position) reads
+                // are all issued before their adds
+                const int c = lane & 15, rq = lane >> 4;
+                const int n = nw + c * 4;
 #pragma unroll
-            for (int it = 0; it < 8; ++it) {
-                const int m = mr + it * 4 + rq;
-                if (m < p.M && n < p.N)
-                    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.C) + int64_t(m) * p.ldc + n) = w[it] + add[it];
-            }
-        } else if (vtile) {
-            if constexpr (EPI == WENC_EPI_QKV) {
-                // V^T [b][h][dim][slot]: the block's 32 rows are two 16-key
-                // groups of one batch item each (the row space is padded to a
-                // multiple of 16 keys).  A run is 8 consecutive slots of one
-                // dimension: slots 16 G + 8 s8 .. +7 hold keys 16 G +
-                // vt_slot(8 s8 + q) (the slot order is an involution).  Four
-                // consecutive lanes cover one dimension's 32 slots; keys at or
-                // past T are written as zeros.
+                for (int h0 = 0; h0 < 8; h0 += 4) {
+                    f32x4 w[4], add[4];
 #pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    const int run = it * 64 + lane;
-                    const int s8 = run & 1, gr = (run >> 1) & 1, e = run >> 2;
-                    const uint32_t mg = uint32_t(mr + 16 * gr);
-                    const uint32_t bb = divu(mg, p.t_div);
-                    const uint32_t t0 = mg - bb * p.t_div.d;
-                    f16x8 o;
+                    for (int it = 0; it < 4; ++it)
+                        w[it] = *reinterpret_cast<const f32x4 *>(stg + (((h0 + it) * 4 + rq) * RS + c * 4) * 4);
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const uint32_t key = vt_slot(uint32_t(8 * s8 + q));
-                        const f16 val = *reinterpret_cast<const f16 *>(stg + ((16 * gr + key) * RS + e) * 2);
-                        o[q] = t0 + key < uint32_t(p.T) ? val : (f16)0.0f;
+                    for (int it = 0; it < 4; ++it) {
+                        const int m = mr + (h0 + it) * 4 + rq;
+                        add[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (m < p.M && n < p.N) {
+                            if constexpr (EPI == WENC_EPI_RESID) {
+                                add[it] = ld4(static_cast<const float *>(p.C) + int64_t(m) * p.ldc + n);
+                            } else {
+                                const uint32_t t = m - divu(m, p.pos_div) * p.pos_div.d;
+                                add[it] = ld4(p.pos + int64_t(t) * p.N + n);
+                            }
+                        }
                     }
-                    if (int(mg) < p.M)
-                        *reinterpret_cast<f16x8 *>(p.vt + ((int64_t(bb) * p.H + vhead) * 64 + e) * p.ldvt + t0 + 8 * s8) = o;
-                }
-                // the last key group of a batch item also clears slots
-                // t_div.d .. ldvt-1 of its 64 dimensions
 #pragma unroll
-                for (int gr = 0; gr < 2; ++gr) {
-                    const uint32_t mg = uint32_t(mr + 16 * gr);
-                    const uint32_t bb = divu(mg, p.t_div);
-                    const uint32_t t0 = mg - bb * p.t_div.d;
-                    if (int(mg) < p.M && t0 + 16 == p.t_div.d) {
-                        const int nz = (p.ldvt - int(p.t_div.d)) / 8;
-                        for (int run = lane; run < nz * 64; run += 64) {
-                            const int e = run & 63, zc = run >> 6;
-                            *reinterpret_cast<f16x8 *>(p.vt + ((int64_t(bb) * p.H + vhead) * 64 + e) * p.ldvt +
-                                                       p.t_div.d + 8 * zc) = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                    for (int it = 0; it < 4; ++it) {
+                        const int m = mr + (h0 + it) * 4 + rq;
+                        if (m < p.M && n < p.N)
+                            *reinterpret_cast<f32x4 *>(static_cast<float *>(p.C) + int64_t(m) * p.ldc + n) = w[it] + add[it];
+                    }
+                }
+            } else if (vtile) {
+                if constexpr (EPI == WENC_EPI_QKV) {
+                    // V^T [b][h][dim][slot]: the block's 32 rows are two 16-key
+                    // groups of one batch item each (the row space is padded to a
+                    // multiple of 16 keys).  A run is 8 consecutive slots of one
+                    // dimension: slots 16 G + 8 s8 .. +7 hold keys 16 G +
+                    // vt_slot(8 s8 + q) (the slot order is an involution).  Four
+                    // consecutive lanes cover one dimension's 32 slots; keys at or
+                    // past T are written as zeros.
+#pragma unroll
+                    for (int it = 0; it < 4; ++it) {
+                        const int run = it * 64 + lane;
+                        const int s8 = run & 1, gr = (run >> 1) & 1, e = run >> 2;
+                        const uint32_t mg = uint32_t(mr + 16 * gr);
+                        const uint32_t bb = divu(mg, p.t_div);
+                        const uint32_t t0 = mg - bb * p.t_div.d;
+                        f16x8 o;
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const uint32_t key = vt_slot(uint32_t(8 * s8 + q));
+                            const f16 val = *reinterpret_cast<const f16 *>(stg + ((16 * gr + key) * RS + e) * 2);
+                            o[q] = t0 + key < uint32_t(p.T) ? val : (f16)0.0f;
+                        }
+                        if (int(mg) < p.M)
+                            *reinterpret_cast<f16x8 *>(p.vt + ((int64_t(bb) * p.H + vhead) * 64 + e) * p.ldvt + t0 + 8 * s8) = o;
+                    }
+                    // the last key group of a batch item also clears slots
+                    // t_div.d .. ldvt-1 of its 64 dimensions
+#pragma unroll
+                    for (int gr = 0; gr < 2; ++gr) {
+                        const uint32_t mg = uint32_t(mr + 16 * gr);
+                        const uint32_t bb = divu(mg, p.t_div);
+                        const uint32_t t0 = mg - bb * p.t_div.d;
+                        if (int(mg) < p.M && t0 + 16 == p.t_div.d) {
+                            const int nz = (p.ldvt - int(p.t_div.d)) / 8;
+                            for (int run = lane; run < nz * 64; run += 64) {
+                                const int e = run & 63, zc = run >> 6;
+                                *reinterpret_cast<f16x8 *>(p.vt + ((int64_t(bb) * p.H + vhead) * 64 + e) * p.ldvt +
+                                                           p.t_div.d + 8 * zc) = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                            }
                         }
                     }
                 }
-            }
-        } else {
-            // 8 lanes per 64-half row, 8 rows per instruction
-            const int c = lane & 7, r8 = lane >> 3;
-            const int n = n0 + wn * WN + c * 8;
+            } else {
+                // 8 lanes per 64-half row, 8 rows per instruction
+                const int c = lane & 7, r8 = lane >> 3;
+                const int n = nw + c * 8;
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const int r = it * 8 + r8;
-                const f16x8 o = *reinterpret_cast<const f16x8 *>(stg + (r * RS + c * 8) * 2);
-                const int m = mr + r;
-                if (m < p.M && n < p.N) epi_row8<EPI>(p, m, n, o);
+                for (int it = 0; it < 4; ++it) {
+                    const int r = it * 8 + r8;
+                    const f16x8 o = *reinterpret_cast<const f16x8 *>(stg + (r * RS + c * 8) * 2);
+                    const int m = mr + r;
+                    if (m < p.M && n < p.N) epi_row8<EPI>(p, m, n, o);
+                }
             }
         }
     }
@@ -603,6 +621,8 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag) {
     int cfg = g_tile_override;
     if (cfg > 1) {
         // 256 x 256 tiles when they fill the 256 CUs nearly twice over
+        // (measured: on 24000 x 768 x {768, 3072}, 282 such tiles, the
+        // 128 x 128 tiles at two workgroups per CU are 10-20% faster)
         const long big = long((p.M + 255) / 256) * ((a.N + 255) / 256);
         cfg = big >= 448 ? 1 : 0;
     }
