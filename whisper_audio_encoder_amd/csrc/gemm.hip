@@ -8,10 +8,10 @@
 // projection (k without bias, model.nu), out_proj and fc2 with the residual
 // add, and fc1 with the erf GELU (kernels.nu).  Matrices are [out][in]
 // (kernels.nu, wk_matvec: W[rows][cols]), so W rows are K-contiguous, which
-// is exactly the operand layout v_mfma_f32_32x32x16_f16 reads per lane.
+// is exactly the operand layout v_mfma_f32_16x16x32_f16 reads per lane.
 //
-// Structure (details at each step below).  A workgroup of NW wave64s owns a BM x BN output tile and walks
-// K in steps of 64.  Each step is moved from global memory straight into LDS
+// Structure (details at each step below).  A workgroup of NW wave64s owns a
+// BM x BN output tile and walks K in steps of 64 (two MFMA k slices of 32).  Each step is moved from global memory straight into LDS
 // by buffer_load ... lds (no VGPR staging); a buffer offset with bit 31 set
 // lies beyond the descriptor's range and reads as zero, which pads the M, N
 // and K tails without branches.  Within LDS, 16-byte chunks are XOR-swizzled
