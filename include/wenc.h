@@ -228,6 +228,17 @@ typedef struct wenc_gemm_args {
 } wenc_gemm_args;
 int wenc_k_gemm(const wenc_gemm_args *args, void *stream);
 
+/* Test-only: the tile configuration of every later GEMM launch in this
+ * process (all handles).  tile: -1 automatic (the default, or the
+ * WENC_GEMM_TILE environment variable when set), 0 = 128 x 128 tiles,
+ * 1 = 256 x 256 tiles.  split: 1 (the default) lets an automatic launch give
+ * its last 256-row tile rows to 128 x 128 tiles when that evens out the last
+ * round over the compute units, 0 keeps one tile size.  Every configuration
+ * sums each output over k in the same order, so all give the same bits.
+ * Not thread-safe against concurrent GEMM launches; returns WENC_EINVAL for
+ * values out of range. */
+int wenc_k_gemm_mode(int32_t tile, int32_t split);
+
 /* Non-causal attention per (batch, head) (kernels.nu, wk_attn with causal 0):
  *   ao[b][t][h*64 + e] = sum_u softmax_u(q[b][h][t] . k[b][h][u]) * v[b][h][u][e]
  * with q ALREADY scaled by log2(e)/sqrt(64) (the softmax is taken in base 2),

@@ -166,6 +166,82 @@ def test_gemm_qkv_scatter(B, T, H, K):
     np.testing.assert_allclose(host(vt).astype(np.float64), ref_vt, rtol=1e-3, atol=1e-4)
 
 
+def _gemm_mode(tile, split):
+    assert wenc.lib().wenc_k_gemm_mode(tile, split) == wenc.WENC_OK
+
+
+# automatic with the last tile rows split off, automatic without, all 256 x 256, all 128 x 128
+GEMM_MODES = [(-1, 1), (-1, 0), (1, 0), (0, 0)]
+
+
+@pytest.mark.parametrize("epi", [wenc.WENC_EPI_GELU_F16, wenc.WENC_EPI_RESID])
+def test_gemm_tile_configs_bitwise(epi):
+    """Every tile configuration, including a launch whose last tile rows go to
+    128 x 128 tiles (24000 x 3072: 1128 256-wide tiles, 85 tile rows kept
+    big), sums each output over k in the same order: the same bits."""
+    M, N, K = 24000, 3072, 256
+    say(f"gemm tile configs epi={epi} M={M} N={N} K={K}")
+    rng = np.random.default_rng(77 + epi)
+    A, W, b = _operands(rng, M, N, K)
+    Ad, Wd, bd = f16_dev(A), f16_dev(W), dev(b)
+    x0 = rng.standard_normal((M, N)).astype(np.float32)
+    outs = []
+    try:
+        for tile, split in GEMM_MODES:
+            _gemm_mode(tile, split)
+            C = dev(x0) if epi == wenc.WENC_EPI_RESID else torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+            _gemm(Ad, Wd, bd, epi, M, N, K, C=C)
+            outs.append(host(C))
+    finally:
+        _gemm_mode(-1, 1)
+    for o in outs[1:]:
+        assert np.array_equal(outs[0], o, equal_nan=True)
+    rows = np.unique(np.r_[np.arange(64), rng.integers(0, M, 128), np.arange(85 * 256 - 8, 85 * 256 + 8), M - 1])
+    pre = _f64(A[rows]) @ _f64(W).T + b
+    if epi == wenc.WENC_EPI_RESID:
+        np.testing.assert_allclose(outs[0][rows], x0[rows] + pre, rtol=1e-5, atol=1e-4)
+    else:
+        np.testing.assert_allclose(outs[0][rows].astype(np.float64), oracle.gelu(pre), rtol=1e-3, atol=1e-4)
+
+
+def test_gemm_qkv_tile_configs_bitwise():
+    """The q|k|v scatter (rows padded to 16 keys per item) under every tile
+    configuration, at the whisper-small shape (16 windows, 12 heads), which
+    splits off its last tile rows: the same bits."""
+    B, T, H, K = 16, 1500, 12, 64
+    say(f"gemm qkv tile configs B={B} T={T} H={H} K={K}")
+    rng = np.random.default_rng(91)
+    d = 64 * H
+    M, N = B * T, 3 * d
+    A, W, b = _operands(rng, M, N, K)
+    b[d:2 * d] = 0
+    Ad, Wd, bd = f16_dev(A), f16_dev(W), dev(b)
+    ldvt = 1536
+    outs = []
+    try:
+        for tile, split in GEMM_MODES:
+            _gemm_mode(tile, split)
+            q = torch.full((B, H, T, 64), float("nan"), dtype=torch.float16, device=DEV)
+            k = torch.full_like(q, float("nan"))
+            vt = torch.full((B, H, 64, ldvt), float("nan"), dtype=torch.float16, device=DEV)
+            _gemm(Ad, Wd, bd, wenc.WENC_EPI_QKV, M, N, K, q=q, k=k, vt=vt, T=T, n_head=H, ldvt=ldvt,
+                  q_scale=LOG2E / 8)
+            outs.append([host(q), host(k), host(vt)])
+    finally:
+        _gemm_mode(-1, 1)
+    for o in outs[1:]:
+        for a, b_ in zip(outs[0], o):
+            assert np.array_equal(a, b_)
+    assert not np.isnan(outs[0][2]).any()  # every V^T slot written
+
+
+def test_gemm_mode_rejects_bad_values():
+    L = wenc.lib()
+    assert L.wenc_k_gemm_mode(2, 1) == wenc.WENC_EINVAL
+    assert L.wenc_k_gemm_mode(-1, 2) == wenc.WENC_EINVAL
+    assert L.wenc_k_gemm_mode(-1, 1) == wenc.WENC_OK
+
+
 @pytest.mark.parametrize("B,F,C,O", [(2, 32, 16, 64), (3, 3000, 80, 384), (1, 10, 8, 128)])
 def test_gemm_conv_stem(B, F, C, O):
     """conv1 (stride 1) and conv2 (stride 2) as GEMMs over overlapping frame

@@ -61,6 +61,7 @@ struct GemmP {
     int H, ldvt, dmodel;
     float q_scale;
     int M, N, K;
+    int m_begin;  // first row this launch covers (rows m_begin .. M-1)
     int tiles_m, tiles_n;
 };
 
@@ -202,7 +203,7 @@ gemm_kernel(const GemmP p) {
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     int tm, tn;
     tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int m0 = p.m_begin + tm * BM, n0 = tn * BN;
 
     // Direct loads: one instruction moves 8 tile rows x 128 B; lane i lands at
     // row r = 8 g + (i >> 3), chunk position i & 7, so it fetches logical
@@ -497,7 +498,7 @@ gemm_kernel(const GemmP p) {
 template <int BM, int BN, int WM, int WN, int NW, int TAG>
 hipError_t launch_cfg(const GemmP &base, int epi, hipStream_t s) {
     GemmP p = base;
-    p.tiles_m = (p.M + BM - 1) / BM;
+    p.tiles_m = (p.M - p.m_begin + BM - 1) / BM;
     p.tiles_n = (p.N + BN - 1) / BN;
     const dim3 grid(p.tiles_m * p.tiles_n), block(NW * 64);
     switch (epi) {
@@ -517,8 +518,33 @@ hipError_t launch_tagged(const GemmP &p, int epi, int tag, hipStream_t s) {
 }
 
 int g_tile_override = -1;  // WENC_GEMM_TILE: 0 = 128x128 x 4 waves, 1 = 256x256 x 8 waves
+int g_split = 1;            // WENC_GEMM_SPLIT=0 keeps a launch on one tile size
+
+// Compute units of the current device (cached per device).
+long cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 }  // namespace
+
+int gemm_mode(int tile, int split) {
+    if (tile < -1 || tile > 1 || split < 0 || split > 1) return -1;
+    if (tile == -1) {
+        const char *e = std::getenv("WENC_GEMM_TILE");
+        tile = e ? std::atoi(e) : 99;
+    }
+    g_tile_override = tile;
+    g_split = split;
+    return 0;
+}
 
 const char *gemm_check(const wenc_gemm_args &a) {
     if (!a.A || !a.W || !a.bias) return "gemm: A, W and bias must be non-null";
@@ -617,19 +643,44 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag) {
     if (g_tile_override < 0) {
         const char *e = std::getenv("WENC_GEMM_TILE");
         g_tile_override = e ? std::atoi(e) : 99;
+        const char *f = std::getenv("WENC_GEMM_SPLIT");
+        g_split = f ? std::atoi(f) : 1;
     }
-    int cfg = g_tile_override;
-    if (cfg > 1) {
-        // 256 x 256 tiles when they fill the 256 CUs nearly twice over
-        // (measured: on 24000 x 768 x {768, 3072}, 282 such tiles, the
-        // 128 x 128 tiles at two workgroups per CU are 10-20% faster)
-        const long big = long((p.M + 255) / 256) * ((a.N + 255) / 256);
-        cfg = big >= 448 ? 1 : 0;
+    if (g_tile_override == 1) return launch_tagged<256, 256, 128, 64, 8>(p, a.epilogue, tag, s);
+    if (g_tile_override == 0) return launch_tagged<128, 128, 64, 64, 4>(p, a.epilogue, tag, s);
+    // 256 x 256 tiles when they fill the CUs nearly twice over (measured: on
+    // 24000 x 768 x {768, 3072}, 282 such tiles, the 128 x 128 tiles at two
+    // workgroups per CU are 10-20% faster).
+    const long tn_big = (p.N + 255) / 256, tm_big = (p.M + 255) / 256;
+    if (tm_big * tn_big < 448) return launch_tagged<128, 128, 64, 64, 4>(p, a.epilogue, tag, s);
+    // The 256 x 256 kernel runs one tile per CU at a time, so a tile count
+    // just past a multiple of the CU count leaves most CUs idle in the last
+    // round.  Then the last tile rows go to the 128 x 128 kernel instead (two
+    // workgroups per CU), whose round costs about 0.6 of a big round; both
+    // kernels sum each output over k in the same order, so the split changes
+    // no result bit.  R = the number of 256-row tile rows kept big.
+    long best_r = tm_big;
+    if (g_split) {
+        const long cus = cu_count();
+        auto rounds = [](long n, long per) { return double((n + per - 1) / per); };
+        double best = rounds(tm_big * tn_big, cus);
+        for (long r = tm_big - 1; r >= 1 && r >= tm_big - 64; --r) {
+            const long small = ((p.M - 256 * r + 127) / 128) * ((p.N + 127) / 128);
+            const double cost = rounds(r * tn_big, cus) + 0.6 * rounds(small, 2 * cus);
+            if (cost < best - 0.05) {
+                best = cost;
+                best_r = r;
+            }
+        }
     }
-    switch (cfg) {
-        case 1: return launch_tagged<256, 256, 128, 64, 8>(p, a.epilogue, tag, s);
-        default: return launch_tagged<128, 128, 64, 64, 4>(p, a.epilogue, tag, s);
-    }
+    if (best_r == tm_big) return launch_tagged<256, 256, 128, 64, 8>(p, a.epilogue, tag, s);
+    GemmP big = p;
+    big.M = int(256 * best_r);
+    const hipError_t e = launch_tagged<256, 256, 128, 64, 8>(big, a.epilogue, tag, s);
+    if (e != hipSuccess) return e;
+    GemmP tail = p;
+    tail.m_begin = int(256 * best_r);
+    return launch_tagged<128, 128, 64, 64, 4>(tail, a.epilogue, tag, s);
 }
 
 }  // namespace wk

@@ -11,6 +11,8 @@ namespace wk {
 const char *gemm_check(const wenc_gemm_args &a);
 // tag 1 selects a separately named copy of the kernel (fc1, fc2).
 hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag = 0);
+// Tile configuration of later launches (see wenc_k_gemm_mode); -1 if out of range.
+int gemm_mode(int tile, int split);
 
 const char *attention_check(int batch, int n_head, int T, int ldvt);
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, uint16_t *ao,

@@ -775,6 +775,11 @@ int wenc_k_gemm(const wenc_gemm_args *args, void *stream) {
     return e == hipSuccess ? WENC_OK : fail(nullptr, WENC_EHIP, "gemm: %s", hipGetErrorString(e));
 }
 
+int wenc_k_gemm_mode(int32_t tile, int32_t split) {
+    if (wk::gemm_mode(tile, split) != 0) return fail(nullptr, WENC_EINVAL, "gemm mode: tile must be -1, 0 or 1 and split 0 or 1");
+    return WENC_OK;
+}
+
 int wenc_k_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, uint16_t *ao, int32_t batch,
                      int32_t n_head, int32_t T, int32_t ldvt, void *stream) {
     if (const char *m = wk::attention_check(batch, n_head, T, ldvt)) return fail(nullptr, WENC_EINVAL, "%s", m);

@@ -100,6 +100,8 @@ def lib() -> ctypes.CDLL:
     L.wenc_k_layernorm.restype = ctypes.c_int
     L.wenc_k_gemm.argtypes = [ctypes.POINTER(wenc_gemm_args), vp]
     L.wenc_k_gemm.restype = ctypes.c_int
+    L.wenc_k_gemm_mode.argtypes = [i32, i32]
+    L.wenc_k_gemm_mode.restype = ctypes.c_int
     L.wenc_k_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp]
     L.wenc_k_attention.restype = ctypes.c_int
     L.wenc_profile.argtypes = [vp, ctypes.c_uint32]
