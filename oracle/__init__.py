@@ -7,6 +7,7 @@ library and its binding) never calls it and shares no code with it.
 from .encoder import (  # noqa: F401
     attention,
     conv1d,
+    cross_attend,
     cross_kv,
     encode,
     encoder_block,

@@ -180,3 +180,26 @@ def cross_kv(memory, x_wk, x_wv, x_bv):
     """
     m = _f64(memory)
     return m @ _f64(x_wk).T, m @ _f64(x_wv).T + _f64(x_bv)
+
+
+def cross_attend(q, xk, xv, n_head: int) -> np.ndarray:
+    """Decoder cross-attention of a decode step's query rows over the cached
+    K/V of one decoder layer (whisper README, "Performance and memory": the
+    one-query attention a generated token runs over the 1500 encoder
+    positions; whisper 0.9.0 API page, wh_prepare_cross: xk and xv hold
+    n_ctx x d_model per decoder layer; kernels.nu: scores q.k / sqrt(hd)).
+
+    q: [n_q, d] (the step's query rows, after q_proj); xk, xv: [T, d].  Head
+    h uses columns [hd*h, hd*(h+1)); every position is visible (the encoder
+    memory has no mask).  Per head: softmax(q_h xk_h^T / sqrt(hd)) xv_h, the
+    definition `attention` evaluates.  Returns [n_q, d] in fp64.
+    """
+    q, xk, xv = _f64(q), _f64(xk), _f64(xv)
+    d = q.shape[1]
+    hd = d // n_head
+    out = np.empty_like(q)
+    for h in range(n_head):
+        c = slice(h * hd, (h + 1) * hd)
+        out[:, c] = attention(q[:, c], xk[:, c], xv[:, c])
+    return out
+

@@ -342,6 +342,71 @@ def test_cross_k_bias_would_be_unobservable():
     np.testing.assert_allclose(oracle.softmax_rows(q @ (K + c).T), oracle.softmax_rows(q @ K.T), atol=1e-12)
 
 
+# ---------------------------------------- decode-step cross-attention (one query)
+def test_cross_attend_brute_force():
+    """Pure-Python softmax over keys per head at a tiny size (2 heads of 4
+    dims, 5 keys, 2 query rows), with the 1/sqrt(hd) scale written out."""
+    rng = np.random.default_rng(31)
+    n_q, T, H, hd = 2, 5, 2, 4
+    q = rng.standard_normal((n_q, H * hd))
+    k = rng.standard_normal((T, H * hd))
+    v = rng.standard_normal((T, H * hd))
+    out = oracle.cross_attend(q, k, v, H)
+    for i in range(n_q):
+        for h in range(H):
+            cols = range(h * hd, (h + 1) * hd)
+            s = [sum(float(q[i, c]) * float(k[u, c]) for c in cols) / math.sqrt(hd) for u in range(T)]
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            z = sum(e)
+            for c in cols:
+                ref = sum(e[u] / z * float(v[u, c]) for u in range(T))
+                assert abs(out[i, c] - ref) < 1e-12
+
+
+def test_cross_attend_matches_torch_sdpa():
+    """torch's scaled_dot_product_attention (fp64, no mask) per head, at the
+    decode-step shape: one query row over 1500 keys, 20 heads of 64."""
+    rng = np.random.default_rng(32)
+    T, H = 1500, 20
+    q = rng.standard_normal((1, 64 * H))
+    k = rng.standard_normal((T, 64 * H))
+    v = rng.standard_normal((T, 64 * H))
+    out = oracle.cross_attend(q, k, v, H)
+    tq = torch.from_numpy(q).view(1, H, 64).transpose(0, 1)
+    tk = torch.from_numpy(k).view(T, H, 64).transpose(0, 1)
+    tv = torch.from_numpy(v).view(T, H, 64).transpose(0, 1)
+    ref = F.scaled_dot_product_attention(tq, tk, tv).transpose(0, 1).reshape(1, 64 * H)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_cross_attend_closed_forms():
+    """One key: the output is that key's value row.  Identical keys: the mean
+    of the values.  A +40 score margin on one key selects its value row.
+    Heads and query rows are independent of each other."""
+    rng = np.random.default_rng(33)
+    H, d = 3, 192
+    q = rng.standard_normal((2, d))
+    v = rng.standard_normal((7, d))
+    np.testing.assert_allclose(oracle.cross_attend(q, rng.standard_normal((1, d)), v[:1], H), np.repeat(v[:1], 2, 0), atol=1e-15)
+    same = np.repeat(rng.standard_normal((1, d)), 7, 0)
+    np.testing.assert_allclose(oracle.cross_attend(q, same, v, H), np.repeat(v.mean(0, keepdims=True), 2, 0), atol=1e-13)
+    k = np.zeros((7, d))
+    qq = np.zeros((1, d))
+    qq[0, :64] = 1.0
+    k[4, :64] = 40 * 8 / 64  # head 0: key 4 scores 40, the others 0
+    got = oracle.cross_attend(qq, k, v, H)
+    np.testing.assert_allclose(got[0, :64], v[4, :64], atol=1e-15)
+    k2 = rng.standard_normal((7, d))
+    k3 = k2.copy()
+    k3[:, 64:128] = rng.standard_normal((7, 64))  # change head 1's keys only
+    a, b = oracle.cross_attend(q, k2, v, H), oracle.cross_attend(q, k3, v, H)
+    np.testing.assert_array_equal(a[:, :64], b[:, :64])
+    np.testing.assert_array_equal(a[:, 128:], b[:, 128:])
+    assert not np.allclose(a[:, 64:128], b[:, 64:128])
+    np.testing.assert_allclose(oracle.cross_attend(q[1:], k2, v, H), a[1:], rtol=1e-13, atol=1e-14)
+
+
 # --------------------------------------------------------------- shapes (P-f)
 def test_family_golden_matches_configs():
     fam = {r[0]: tuple(map(int, r[1:])) for r in read_golden("whisper_family.txt")}
