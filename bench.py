@@ -54,6 +54,8 @@ def site_work(cfg, B):
         "xcvt": ("hbm", M * d * (4.0 + 2.0)),
         # log-mel: per frame, the DFT as a contraction (400 samples x 201 bins x (cos, sin)) and the filters
         "mel": ("mfma", 2.0 * B * F * (2 * 400 * 201 + 201 * nm)),
+        # decode-step cross-attention, per decoder layer: K and V read once (fp16)
+        "xatt": ("hbm", 2.0 * M * d * 2.0),
     }
 
 
@@ -216,8 +218,34 @@ def time_cross(enc, model, memory, n_dec, steps):
     wenc.wenc_profile(enc.h, 0)
     flops = 2.0 * B * T * 2 * d * d * n_dec
     log(f"[bench] cross K/V, {n_dec} decoder layers: {ms:.3f} ms per call, {flops / ms / 1e9:.1f} TFLOP/s")
+    # one decode step's cross-attention: a query row per window over every
+    # layer's cached K/V (HBM-bound: K and V read once)
+    q = (torch.randn((B, 1, d), device=memory.device) * 0.5).half()
+    o = torch.empty_like(q)
+    for layer in range(n_dec):
+        enc.cross_attend(q, xk[layer], xv[layer], out=o)
+    wenc.wenc_profile(enc.h, 1 << wenc.SITES.index("xatt"))
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        for layer in range(n_dec):
+            enc.cross_attend(q, xk[layer], xv[layer], out=o)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / steps
+    at_ms, at_n = wenc.wenc_profile_read(enc.h)["xatt"]
+    wenc.wenc_profile(enc.h, 0)
+    per_layer = at_ms / max(at_n, 1)
+    kv_bytes = 2.0 * B * T * d * 2  # K and V, fp16, one layer
+    log(f"[bench] decode-step cross-attention, {n_dec} layers: {step_ms:.3f} ms per step, "
+        f"{per_layer * 1e3:.1f} us per layer ({kv_bytes / (per_layer * 1e-3) / 1e9:.0f} GB/s of K/V)")
     return {"n_dec_layer": n_dec, "ms_per_call": ms, "tflops": flops / ms / 1e9,
-            "gemm_avg_launch_ms": kv_ms / max(kv_n, 1)}
+            "gemm_avg_launch_ms": kv_ms / max(kv_n, 1),
+            "decode_step_attention": {"n_q": 1, "ms_per_step": step_ms, "us_per_layer": per_layer * 1e3,
+                                      "kv_gb_per_s": kv_bytes / (per_layer * 1e-3) / 1e9,
+                                      "roofline": {"bound": "hbm", "achieved": kv_bytes / (per_layer * 1e-3) / 1e9,
+                                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                                   "frac": kv_bytes / (per_layer * 1e-3) / 1e9 / PEAK_HBM_GBS}}}
 
 
 def main(argv=None):

@@ -228,6 +228,26 @@ typedef struct wenc_gemm_args {
 } wenc_gemm_args;
 int wenc_k_gemm(const wenc_gemm_args *args, void *stream);
 
+/* Decode-step cross-attention over one decoder layer's cached K/V: the
+ * attention a generated token runs over the n_ctx encoder positions (whisper
+ * README, "Performance and memory": one query, the keys split across
+ * blocks and the partial softmaxes merged; whisper 0.9.0 API page,
+ * wh_prepare_cross: per layer xk, xv of n_ctx x d_model; kernels.nu:
+ * scores q.k / sqrt(64)).  For batch item b, query row i and head h
+ * (columns [64h, 64h + 64)):
+ *   out[b][i][h] = sum_u softmax_u(q[b][i][h] . xk[b][u][h] / 8) xv[b][u][h]
+ * over u < n_ctx, no mask.  q, out: device fp16 [batch][n_q][d_model]
+ * (q after q_proj); xk, xv: device fp16 [batch][n_ctx][d_model], e.g. one
+ * decoder layer's slice of wenc_prepare_cross's output; all four 16-byte
+ * aligned, caller-owned.  1 <= n_q <= 8 (queries per sequence: one for
+ * greedy decoding, a few for beams), 1 <= n_ctx <= cfg.n_ctx, batch >= 0
+ * (chunked through the handle's activation scratch, which it shares with
+ * wenc_forward: one call at a time per handle).  Scores, probabilities and
+ * sums are fp32; out is rounded to fp16 once.  Enqueues on `stream`, no
+ * host sync.  EINVAL for bad sizes, NULL or misaligned pointers. */
+int wenc_cross_attend(wenc_t *h, const void *q, const void *xk, const void *xv, int32_t batch, int32_t n_q,
+                      int32_t n_ctx, void *out, void *stream);
+
 /* Test-only: the tile configuration of every later GEMM launch in this
  * process (all handles).  tile: -1 automatic (the default, or the
  * WENC_GEMM_TILE environment variable when set), 0 = 128 x 128 tiles,
@@ -253,13 +273,14 @@ int wenc_k_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, u
 /* Per-launch timing of wenc_forward, wenc_prepare_cross and wenc_log_mel
  * with HIP events recorded on the caller's stream around the launches whose
  * site bit is set in `site_mask`
+ * (and wenc_cross_attend)
  * (bit s = 1 << WENC_SITE_*); 0 turns it off.  Events are read, and cleared,
  * by wenc_profile_read (which synchronises on them). */
 enum {
     WENC_SITE_INGEST = 0, WENC_SITE_CONV1 = 1, WENC_SITE_CONV2 = 2, WENC_SITE_LN1 = 3,
     WENC_SITE_QKV = 4, WENC_SITE_ATTN = 5, WENC_SITE_OPROJ = 6, WENC_SITE_LN2 = 7,
     WENC_SITE_FC1 = 8, WENC_SITE_FC2 = 9, WENC_SITE_LNF = 10, WENC_SITE_XCVT = 11,
-    WENC_SITE_XKV = 12, WENC_SITE_MEL = 13, WENC_N_SITES = 14
+    WENC_SITE_XKV = 12, WENC_SITE_MEL = 13, WENC_SITE_XATT = 14, WENC_N_SITES = 15
 };
 int wenc_profile(wenc_t *h, uint32_t site_mask);
 /* ms_total[s] and launches[s] for s < WENC_N_SITES (arrays of that length). */

@@ -36,6 +36,15 @@ const char *logmel_check(int batch, int n_frames, int n_mels);
 hipError_t launch_logmel(const float *audio, int batch, int n_frames, const float *tab, const float *win,
                          const float *filt, int n_mels, float *out, float *blkmax, hipStream_t s);
 
+// Decode-step cross-attention (xattn.hip): q fp16 [batch][n_q][64 n_head],
+// xk, xv fp16 [batch][T][64 n_head] (16-byte aligned), out fp16 like q;
+// part: fp32 workspace of xattn_part_bytes(batch, n_head, n_q, T) bytes.
+constexpr int XATTN_MAX_Q = 8;
+size_t xattn_part_bytes(int batch, int n_head, int n_q, int T);
+const char *xattn_check(int batch, int n_head, int n_q, int T);
+hipError_t launch_xattn(const uint16_t *q, const uint16_t *xk, const uint16_t *xv, uint16_t *out, float *part,
+                        int batch, int n_head, int n_q, int T, hipStream_t s);
+
 // y fp16 [n] = x fp32 [n] rounded to nearest even; n % 4 == 0, 16-byte aligned.
 hipError_t launch_to_f16(const float *x, uint16_t *y, int64_t n, hipStream_t s);
 

@@ -717,6 +717,38 @@ int wenc_prepare_cross(wenc_t *h, const float *memory, int32_t batch, int32_t n_
     return WENC_OK;
 }
 
+int wenc_cross_attend(wenc_t *h, const void *q, const void *xk, const void *xv, int32_t batch, int32_t n_q,
+                      int32_t n_ctx, void *out, void *stream) {
+    if (!h) return fail(nullptr, WENC_EINVAL, "wenc_cross_attend: handle is NULL");
+    const wenc_config &c = h->cfg;
+    if (const char *m = wk::xattn_check(batch, c.n_head, n_q, n_ctx))
+        return fail(&h->err, WENC_EINVAL, "wenc_cross_attend: %s", m);
+    if (n_ctx > c.n_ctx) return fail(&h->err, WENC_EINVAL, "wenc_cross_attend: n_ctx %d > %d", n_ctx, c.n_ctx);
+    if (batch == 0) return WENC_OK;
+    if (!q || !xk || !xv || !out) return fail(&h->err, WENC_EINVAL, "wenc_cross_attend: null pointer");
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(xk) | reinterpret_cast<uintptr_t>(xv) |
+         reinterpret_cast<uintptr_t>(out)) & 15)
+        return fail(&h->err, WENC_EINVAL, "wenc_cross_attend: q, xk, xv and out must be 16-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int d = c.d_model;
+    // the partials live in the fp16 LayerNorm-output region of the scratch
+    const size_t room = size_t(2) * c.max_batch * c.n_ctx * d;
+    const size_t per = wk::xattn_part_bytes(1, c.n_head, n_q, n_ctx);
+    if (per > room) return fail(&h->err, WENC_EINVAL, "wenc_cross_attend: the scratch cannot hold one item's partials");
+    const int cap = int(std::max<size_t>(1, std::min<size_t>(room / per, size_t(batch))));
+    float *part = h->S<float>(h->sl.xn);
+    for (int b0 = 0; b0 < batch; b0 += cap) {
+        const int nb = batch - b0 < cap ? batch - b0 : cap;
+        const size_t qo = size_t(b0) * n_q * d, ko = size_t(b0) * n_ctx * d;
+        WENC_TRY(h->site(WENC_SITE_XATT, st, [&] {
+            return wk::launch_xattn(static_cast<const uint16_t *>(q) + qo, static_cast<const uint16_t *>(xk) + ko,
+                                    static_cast<const uint16_t *>(xv) + ko, static_cast<uint16_t *>(out) + qo, part, nb,
+                                    c.n_head, n_q, n_ctx, st);
+        }));
+    }
+    return WENC_OK;
+}
+
 int wenc_log_mel(wenc_t *h, const float *audio, int32_t batch, float *mel, void *stream) {
     if (!h) return fail(nullptr, WENC_EINVAL, "wenc_log_mel: handle is NULL");
     const wenc_config &c = h->cfg;

@@ -1,0 +1,236 @@
+// Decode-step cross-attention over the cached encoder K/V, for gfx950.
+//
+// A decoder step has one query per sequence (a few with beams), and every
+// decoder layer attends over the n_ctx (1500) encoder positions through the
+// K/V that wenc_prepare_cross cached once per clip (whisper 0.9.0 API page,
+// wh_prepare_cross; model.nu: x_wk, x_wv).  Per (batch item, head h, query):
+//   out = softmax_u(q . xk[u] / sqrt(64)) xv[u]
+// over columns [64h, 64h + 64) (kernels.nu: scores q.k / sqrt(hd)).  With one
+// query the encoder's kernel, which amortises each key tile over 128 queries,
+// would leave the chip idle; the whisper README ("Performance and memory")
+// describes the remedy its one-query kernel uses: split the keys across
+// workgroups and merge the partial softmaxes.  The layout below is our own.
+//
+// Pass 1 (xattn_partial): a workgroup takes 64 keys per wave of one (b, h); each
+// lane scores one key against every query (the key row, 128 bytes, in
+// registers; dot products as fp16 pairs accumulated in fp32), a wave takes
+// its maximum and exp2 sum, then accumulates P.V with 8 lanes per value row
+// (8 dimensions each; the rows were loaded before the scores); the
+// waves merge through LDS and write the workgroup's (max, sum, o[64]) per
+// query.  Pass 2
+// (xattn_merge): one wave per (b, h) rescales the partials to a common
+// maximum and sums them in key order, so the result does not depend on
+// scheduling.  The work is bound by reading K and V once (HBM).
+#include "common.h"
+#include "kernels.h"
+
+namespace wk {
+
+namespace {
+
+constexpr int XNW = 4;          // waves per workgroup of pass 1
+constexpr int XKC = 64 * XNW;  // keys per workgroup of pass 1
+constexpr int XPART = 68;  // floats per partial: max, sum, o[64], 2 pad (16-byte rows)
+constexpr float LOG2E_8 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ float wave_add(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+template <int NQ>
+__global__ void __launch_bounds__(64 * XNW)
+xattn_partial(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *__restrict__ xv,
+              float *__restrict__ part, int T, int H, int nc) {
+    const int wg = blockIdx.x;
+    const int c = wg % nc, bh = wg / nc;
+    const int h = bh % H, b = bh / H;
+    const int64_t d = int64_t(H) * 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    __shared__ f16x2 qs[NQ][32];      // the queries of (b, h), fp16 pairs
+    __shared__ float ps[XNW][NQ][64];  // probabilities, by wave and key
+    __shared__ float wm[XNW][NQ], wl[XNW][NQ];
+    __shared__ float wo[XNW][NQ][64];
+
+    for (int i = tid; i < NQ * 32; i += 64 * XNW) {
+        const int qi = i / 32, e2 = i % 32;
+        qs[qi][e2] = *reinterpret_cast<const f16x2 *>(q + (int64_t(b) * NQ + qi) * d + h * 64 + 2 * e2);
+    }
+    __syncthreads();
+
+    // scores: lane = one key of this wave's 64 (base-2, scaled by log2(e)/8).
+    // The wave's 64 value rows are loaded up front (lane: rows 8 it + (lane
+    // >> 3), dimensions 8 (lane & 7) .. +7), so they are in flight while the
+    // scores are formed.
+    const int key0 = c * XKC + wave * 64;
+    const int u = key0 + lane;
+    const int dq = lane & 7, r8 = lane >> 3;
+    f16x8 vv[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int uu = key0 + 8 * it + r8;
+        vv[it] = uu < T ? *reinterpret_cast<const f16x8 *>(xv + (int64_t(b) * T + uu) * d + h * 64 + 8 * dq)
+                        : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    float s[NQ];
+    if (u < T) {
+        const f16 *kr = xk + (int64_t(b) * T + u) * d + h * 64;
+        f16x8 kv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kv[j] = *reinterpret_cast<const f16x8 *>(kr + 8 * j);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    acc = __builtin_amdgcn_fdot2(f16x2{kv[j][2 * t], kv[j][2 * t + 1]}, qs[i][4 * j + t], acc, false);
+            s[i] = acc * LOG2E_8;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) s[i] = -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const float m = wave_max(s[i]);  // -inf only when every key of the wave is past T
+        const float p = u < T ? __builtin_amdgcn_exp2f(s[i] - m) : 0.f;
+        const float l = wave_add(p);
+        ps[wave][i][lane] = p;
+        if (lane == 0) {
+            wm[wave][i] = m;
+            wl[wave][i] = l;
+        }
+    }
+    // ps is written and read by the same wave: LDS operations of a wave
+    // complete in order.  P.V over the wave's rows, then a sum over the 8
+    // lanes that share a dimension group (lane bits 3..5).
+    float oa[NQ][8];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oa[i][e] = 0.f;
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const float p = ps[wave][i][8 * it + r8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) oa[i][e] = fmaf(p, float(vv[it][e]), oa[i][e]);
+        }
+#pragma unroll
+    for (int i = 0; i < NQ; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            oa[i][e] += __shfl_xor(oa[i][e], 8);
+            oa[i][e] += __shfl_xor(oa[i][e], 16);
+            oa[i][e] += __shfl_xor(oa[i][e], 32);
+        }
+    if (r8 == 0) {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wo[wave][i][8 * dq + e] = oa[i][e];
+    }
+    __syncthreads();
+
+    // the workgroup's partial per query: its waves at a common maximum
+    // (a wave whose keys all lie past T has maximum -inf and weight 0)
+    for (int idx = tid; idx < NQ * 64; idx += 64 * XNW) {
+        const int i = idx / 64, e = idx % 64;
+        float M = wm[0][i];
+#pragma unroll
+        for (int w = 1; w < XNW; ++w) M = fmaxf(M, wm[w][i]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < XNW; ++w) {
+            const float sc = __builtin_amdgcn_exp2f(wm[w][i] - M);
+            L = fmaf(sc, wl[w][i], L);
+            O = fmaf(sc, wo[w][i][e], O);
+        }
+        float *pp = part + ((int64_t(bh) * nc + c) * NQ + i) * XPART;
+        pp[2 + e] = O;
+        if (e == 0) {
+            pp[0] = M;
+            pp[1] = L;
+        }
+    }
+}
+
+// One wave per (b, h): out = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c,
+// in key-chunk order.
+template <int NQ>
+__global__ void __launch_bounds__(64)
+xattn_merge(const float *__restrict__ part, f16 *__restrict__ out, int H, int nc) {
+    const int bh = blockIdx.x, e = threadIdx.x;
+    const int h = bh % H, b = bh / H;
+    const int64_t d = int64_t(H) * 64;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const float *p0 = part + (int64_t(bh) * nc * NQ + i) * XPART;
+        float M = p0[0];
+        for (int c = 1; c < nc; ++c) M = fmaxf(M, p0[int64_t(c) * NQ * XPART]);
+        float L = 0.f, O = 0.f;
+        for (int c = 0; c < nc; ++c) {
+            const float *pc = p0 + int64_t(c) * NQ * XPART;
+            const float sc = __builtin_amdgcn_exp2f(pc[0] - M);
+            L = fmaf(sc, pc[1], L);
+            O = fmaf(sc, pc[2 + e], O);
+        }
+        out[(int64_t(b) * NQ + i) * d + h * 64 + e] = f16(O / L);
+    }
+}
+
+template <int NQ>
+hipError_t xattn_dispatch(const f16 *q, const f16 *xk, const f16 *xv, f16 *out, float *part, int B, int H, int T,
+                          hipStream_t s) {
+    const int nc = (T + XKC - 1) / XKC;
+    xattn_partial<NQ><<<dim3(unsigned(B * H * nc)), dim3(64 * XNW), 0, s>>>(q, xk, xv, part, T, H, nc);
+    xattn_merge<NQ><<<dim3(unsigned(B * H)), dim3(64), 0, s>>>(part, out, H, nc);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t xattn_part_bytes(int batch, int n_head, int n_q, int T) {
+    const size_t nc = size_t(T + XKC - 1) / XKC;
+    return size_t(batch) * n_head * nc * n_q * XPART * sizeof(float);
+}
+
+const char *xattn_check(int batch, int n_head, int n_q, int T) {
+    if (batch < 0 || n_head <= 0) return "cross attention: need batch >= 0, n_head > 0";
+    if (n_q < 1 || n_q > XATTN_MAX_Q) return "cross attention: n_q must be in [1, 8]";
+    if (T < 1) return "cross attention: n_ctx must be >= 1";
+    if (int64_t(batch) * n_head * ((T + XKC - 1) / XKC) >= (int64_t(1) << 31)) return "cross attention: grid too large";
+    return nullptr;
+}
+
+hipError_t launch_xattn(const uint16_t *q, const uint16_t *xk, const uint16_t *xv, uint16_t *out, float *part,
+                        int batch, int n_head, int n_q, int T, hipStream_t s) {
+    if (batch == 0) return hipSuccess;
+    const f16 *q16 = reinterpret_cast<const f16 *>(q), *k16 = reinterpret_cast<const f16 *>(xk),
+              *v16 = reinterpret_cast<const f16 *>(xv);
+    f16 *o16 = reinterpret_cast<f16 *>(out);
+    switch (n_q) {
+        case 1: return xattn_dispatch<1>(q16, k16, v16, o16, part, batch, n_head, T, s);
+        case 2: return xattn_dispatch<2>(q16, k16, v16, o16, part, batch, n_head, T, s);
+        case 3: return xattn_dispatch<3>(q16, k16, v16, o16, part, batch, n_head, T, s);
+        case 4: return xattn_dispatch<4>(q16, k16, v16, o16, part, batch, n_head, T, s);
+        case 5: return xattn_dispatch<5>(q16, k16, v16, o16, part, batch, n_head, T, s);
+        case 6: return xattn_dispatch<6>(q16, k16, v16, o16, part, batch, n_head, T, s);
+        case 7: return xattn_dispatch<7>(q16, k16, v16, o16, part, batch, n_head, T, s);
+        case 8: return xattn_dispatch<8>(q16, k16, v16, o16, part, batch, n_head, T, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace wk

@@ -26,7 +26,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 WENC_OK, WENC_EINVAL, WENC_ENOMEM, WENC_ENODEV, WENC_ESTATE, WENC_EHIP = 0, -1, -2, -3, -4, -5
 WENC_TAP_C1, WENC_TAP_STEM, WENC_TAP_BLOCK = 0, 1, 2
 WENC_EPI_GELU_F16, WENC_EPI_CONV2, WENC_EPI_RESID, WENC_EPI_QKV, WENC_EPI_KV = 0, 1, 2, 3, 4
-SITES = ("ingest", "conv1", "conv2", "ln1", "qkv", "attn", "oproj", "ln2", "fc1", "fc2", "lnf", "xcvt", "xkv", "mel")
+SITES = ("ingest", "conv1", "conv2", "ln1", "qkv", "attn", "oproj", "ln2", "fc1", "fc2", "lnf", "xcvt", "xkv", "mel", "xatt")
 N_SITES = len(SITES)
 
 
@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.wenc_load_cross.argtypes = [vp, i32, vp, sz]
     L.wenc_load_cross.restype = ctypes.c_int
     L.wenc_prepare_cross.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+    L.wenc_cross_attend.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
+    L.wenc_cross_attend.restype = ctypes.c_int
     L.wenc_prepare_cross.restype = ctypes.c_int
     L.wenc_log_mel.argtypes = [vp, vp, i32, vp, vp]
     L.wenc_log_mel.restype = ctypes.c_int
@@ -186,6 +188,11 @@ def wenc_load_cross(h, n_dec_layer: int, blob: np.ndarray) -> None:
 def wenc_prepare_cross(h, memory: torch.Tensor, batch: int, n_ctx: int, xk: torch.Tensor, xv: torch.Tensor,
                        stream=None) -> None:
     _check(lib().wenc_prepare_cross(h, _ptr(memory), batch, n_ctx, _ptr(xk), _ptr(xv), _stream(stream)), h)
+
+
+def wenc_cross_attend(h, q: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, batch: int, n_q: int, n_ctx: int,
+                      out: torch.Tensor, stream=None) -> None:
+    _check(lib().wenc_cross_attend(h, _ptr(q), _ptr(xk), _ptr(xv), batch, n_q, n_ctx, _ptr(out), _stream(stream)), h)
 
 
 def wenc_forward_tap(h, mel: torch.Tensor, batch: int, tap: int, dst: torch.Tensor, stream=None) -> None:
@@ -294,6 +301,22 @@ class Encoder:
         xv = torch.empty_like(xk)
         wenc_prepare_cross(self.h, memory, B, T, xk, xv, stream)
         return xk, xv
+
+    def cross_attend(self, q: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, out=None, stream=None):
+        """Decode-step cross-attention of q [batch, n_q, d_model] fp16 over
+        one decoder layer's xk, xv [batch, n_ctx, d_model] fp16 (a slice of
+        prepare_cross's output): fp16 [batch, n_q, d_model]."""
+        c = self.cfg
+        for name, t in (("q", q), ("xk", xk), ("xv", xv)):
+            if not (t.is_cuda and t.dtype == torch.float16 and t.is_contiguous() and t.dim() == 3
+                    and t.shape[2] == c.d_model):
+                raise ValueError(f"{name} must be a contiguous fp16 device tensor [batch, rows, d_model]")
+        if xk.shape != xv.shape or xk.shape[0] != q.shape[0]:
+            raise ValueError("xk and xv must match, with q's batch")
+        if out is None:
+            out = torch.empty_like(q)
+        wenc_cross_attend(self.h, q, xk, xv, q.shape[0], q.shape[1], xk.shape[1], out, stream)
+        return out
 
     def tap(self, mel: torch.Tensor, tap: int, stream=None) -> torch.Tensor:
         self._check_mel(mel)
