@@ -12,6 +12,7 @@ from .encoder import (  # noqa: F401
     encode,
     encoder_block,
     gelu,
+    greedy_argmax,
     layer_norm,
     mha,
     softmax_rows,

@@ -203,3 +203,27 @@ def cross_attend(q, xk, xv, n_head: int) -> np.ndarray:
         out[:, c] = attention(q[:, c], xk[:, c], xv[:, c])
     return out
 
+
+
+def greedy_argmax(logits) -> np.ndarray:
+    """Greedy decoding's token choice per row of logits (whisper README,
+    "Performance and memory": the argmax over the 51865 logits of a step is
+    reduced on the device and only the winning index comes back).
+
+    logits: [rows, n_vocab] (fp32 on the GPU side; widened to fp64, which
+    preserves every comparison).  Per row, the definition: the smallest index
+    whose value equals the row's maximum.  Readings where the pages say
+    nothing: ties go to the smallest index; -0.0 and +0.0 are equal (IEEE
+    comparison); a NaN counts as larger than every number, so the first NaN
+    wins.  Returns int64 [rows].
+    """
+    x = _f64(np.atleast_2d(logits))
+    out = np.empty(x.shape[0], dtype=np.int64)
+    for r in range(x.shape[0]):
+        row = x[r]
+        nan = np.flatnonzero(np.isnan(row))
+        if nan.size:
+            out[r] = nan[0]
+        else:
+            out[r] = np.flatnonzero(row == row.max())[0]
+    return out

@@ -407,6 +407,60 @@ def test_cross_attend_closed_forms():
     np.testing.assert_allclose(oracle.cross_attend(q[1:], k2, v, H), a[1:], rtol=1e-13, atol=1e-14)
 
 
+def test_greedy_argmax_brute_force():
+    """A pure-Python scan (keep the first strictly larger value) over small
+    integer-valued rows, where ties are common."""
+    rng = np.random.default_rng(41)
+    x = rng.integers(-2, 3, size=(50, 9)).astype(np.float32)
+    got = oracle.greedy_argmax(x)
+    for r in range(x.shape[0]):
+        best = 0
+        for i in range(1, x.shape[1]):
+            if float(x[r, i]) > float(x[r, best]):
+                best = i
+        assert got[r] == best
+
+
+def test_greedy_argmax_matches_numpy():
+    """numpy.argmax (first occurrence of the maximum; a NaN wins at its
+    first position) at the decode shape: 16 rows of 51865 fp32 logits, with
+    planted ties and NaNs."""
+    rng = np.random.default_rng(42)
+    x = (4 * rng.standard_normal((16, 51865))).astype(np.float32)
+    x[3, [100, 7000, 51864]] = 99.0
+    x[5, 40000] = np.nan
+    x[6, [10, 20]] = np.nan
+    x[7] = x[7].max()
+    np.testing.assert_array_equal(oracle.greedy_argmax(x), np.argmax(x, axis=1))
+    assert oracle.greedy_argmax(x)[3] == 100
+
+
+def test_greedy_argmax_closed_forms():
+    """Constant, one-hot, monotone rows; signed zeros compare equal; -inf and
+    +inf; NaN beats everything; adjacent fp32 values are told apart; the
+    largest finite and the smallest subnormal magnitudes."""
+    f = np.float32
+    cases = [
+        (np.full(7, 1.5, f), 0),
+        (np.eye(1, 11, 6, dtype=f)[0], 6),
+        (np.arange(13, dtype=f), 12),
+        (np.arange(13, dtype=f)[::-1].copy(), 0),
+        (np.array([-0.0, 0.0], f), 0),
+        (np.array([0.0, -0.0], f), 0),
+        (np.array([-1.0, -0.0, 0.0], f), 1),
+        (np.full(5, -np.inf, f), 0),
+        (np.array([-np.inf, np.inf, np.inf], f), 1),
+        (np.array([1e30, 2.0, 3e38, np.nan, 5.0], f), 3),
+        (np.array([np.nan, np.nan], f), 0),
+        (np.array([1.0, np.nextafter(f(1.0), f(2.0))], f), 1),
+        (np.array([-3e38, 3.4e38, -np.inf], f), 1),
+        (np.array([0.0, 1e-45, -1e-45], f), 1),
+    ]
+    for row, want in cases:
+        assert oracle.greedy_argmax(row[None])[0] == want, (row, want)
+    assert oracle.greedy_argmax(np.zeros((0, 4), f)).shape == (0,)
+
+
 # --------------------------------------------------------------- shapes (P-f)
 def test_family_golden_matches_configs():
     fam = {r[0]: tuple(map(int, r[1:])) for r in read_golden("whisper_family.txt")}
