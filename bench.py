@@ -26,6 +26,7 @@ sys.path.insert(0, HERE)
 METRIC = "encoder 30s-windows/sec and TFLOP/s (% of fp16 MFMA peak), 1 MI355X"
 PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+N_VOCAB = 51865            # Whisper's vocabulary: the logits a greedy decode step reduces
 
 
 def log(*a):
@@ -56,6 +57,8 @@ def site_work(cfg, B):
         "mel": ("mfma", 2.0 * B * F * (2 * 400 * 201 + 201 * nm)),
         # decode-step cross-attention, per decoder layer: K and V read once (fp16)
         "xatt": ("hbm", 2.0 * M * d * 2.0),
+        # greedy argmax of a decode step: one row of N_VOCAB fp32 logits per window, read once
+        "amax": ("hbm", B * N_VOCAB * 4.0),
     }
 
 
@@ -239,13 +242,33 @@ def time_cross(enc, model, memory, n_dec, steps):
     kv_bytes = 2.0 * B * T * d * 2  # K and V, fp16, one layer
     log(f"[bench] decode-step cross-attention, {n_dec} layers: {step_ms:.3f} ms per step, "
         f"{per_layer * 1e3:.1f} us per layer ({kv_bytes / (per_layer * 1e-3) / 1e9:.0f} GB/s of K/V)")
+    # the step's greedy token choice: argmax over N_VOCAB fp32 logits per window
+    logits = torch.randn((B, N_VOCAB), device=memory.device)
+    tok = enc.argmax(logits)
+    wenc.wenc_profile(enc.h, 1 << wenc.SITES.index("amax"))
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        enc.argmax(logits, out=tok)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    am_call_ms = e0.elapsed_time(e1) / steps
+    am_ms, am_n = wenc.wenc_profile_read(enc.h)["amax"]
+    wenc.wenc_profile(enc.h, 0)
+    am_launch = am_ms / max(am_n, 1)
+    am_bytes = B * N_VOCAB * 4.0
+    log(f"[bench] decode-step argmax over {N_VOCAB} logits x {B} rows: {am_launch * 1e3:.1f} us per call "
+        f"({am_bytes / (am_launch * 1e-3) / 1e9:.0f} GB/s)")
     return {"n_dec_layer": n_dec, "ms_per_call": ms, "tflops": flops / ms / 1e9,
             "gemm_avg_launch_ms": kv_ms / max(kv_n, 1),
             "decode_step_attention": {"n_q": 1, "ms_per_step": step_ms, "us_per_layer": per_layer * 1e3,
                                       "kv_gb_per_s": kv_bytes / (per_layer * 1e-3) / 1e9,
                                       "roofline": {"bound": "hbm", "achieved": kv_bytes / (per_layer * 1e-3) / 1e9,
                                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                                   "frac": kv_bytes / (per_layer * 1e-3) / 1e9 / PEAK_HBM_GBS}}}
+                                                   "frac": kv_bytes / (per_layer * 1e-3) / 1e9 / PEAK_HBM_GBS}},
+            "decode_step_argmax": {"rows": B, "n_vocab": N_VOCAB, "us_per_call": am_launch * 1e3,
+                                   "us_per_call_stream": am_call_ms * 1e3,
+                                   "gb_per_s": am_bytes / (am_launch * 1e-3) / 1e9}}
 
 
 def main(argv=None):

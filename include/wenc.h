@@ -248,6 +248,22 @@ int wenc_k_gemm(const wenc_gemm_args *args, void *stream);
 int wenc_cross_attend(wenc_t *h, const void *q, const void *xk, const void *xv, int32_t batch, int32_t n_q,
                       int32_t n_ctx, void *out, void *stream);
 
+/* Greedy token choice on the device: per row, the index of the largest
+ * logit, so that a decode step returns one integer per sequence instead of
+ * the whole vocabulary (whisper README, "Performance and memory": greedy
+ * decoding's argmax over the 51865 logits, reduced on the device).
+ *   out[r] = min { i : logits[r][i] = max_j logits[r][j] }
+ * Ties go to the smallest index; -0.0 equals +0.0; a NaN counts as larger
+ * than every number (the first NaN wins).  logits: device fp32
+ * [rows][ld] (row r at logits + r * ld), out: device int32 [rows]; both
+ * 4-byte aligned, caller-owned.  1 <= n_vocab <= 2^30, ld >= n_vocab,
+ * rows >= 0 (the per-chunk keys go to the handle's activation scratch,
+ * which it shares with wenc_forward: one call at a time per handle).
+ * Exact: no arithmetic, only comparisons.  Enqueues on `stream`, no host
+ * sync.  EINVAL for bad sizes, NULL or misaligned pointers. */
+int wenc_argmax(wenc_t *h, const float *logits, int32_t rows, int32_t n_vocab, int64_t ld, int32_t *out,
+                void *stream);
+
 /* Test-only: the tile configuration of every later GEMM launch in this
  * process (all handles).  tile: -1 automatic (the default, or the
  * WENC_GEMM_TILE environment variable when set), 0 = 128 x 128 tiles,
@@ -273,14 +289,15 @@ int wenc_k_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, u
 /* Per-launch timing of wenc_forward, wenc_prepare_cross and wenc_log_mel
  * with HIP events recorded on the caller's stream around the launches whose
  * site bit is set in `site_mask`
- * (and wenc_cross_attend)
+ * (and wenc_cross_attend, wenc_argmax)
  * (bit s = 1 << WENC_SITE_*); 0 turns it off.  Events are read, and cleared,
  * by wenc_profile_read (which synchronises on them). */
 enum {
     WENC_SITE_INGEST = 0, WENC_SITE_CONV1 = 1, WENC_SITE_CONV2 = 2, WENC_SITE_LN1 = 3,
     WENC_SITE_QKV = 4, WENC_SITE_ATTN = 5, WENC_SITE_OPROJ = 6, WENC_SITE_LN2 = 7,
     WENC_SITE_FC1 = 8, WENC_SITE_FC2 = 9, WENC_SITE_LNF = 10, WENC_SITE_XCVT = 11,
-    WENC_SITE_XKV = 12, WENC_SITE_MEL = 13, WENC_SITE_XATT = 14, WENC_N_SITES = 15
+    WENC_SITE_XKV = 12, WENC_SITE_MEL = 13, WENC_SITE_XATT = 14, WENC_SITE_ARGMAX = 15,
+    WENC_N_SITES = 16
 };
 int wenc_profile(wenc_t *h, uint32_t site_mask);
 /* ms_total[s] and launches[s] for s < WENC_N_SITES (arrays of that length). */

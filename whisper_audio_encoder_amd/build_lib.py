@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwenc.so")
 
-SOURCES = ["gemm.hip", "attention.hip", "layernorm.hip", "frontend.hip", "xattn.hip", "wenc_runtime.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "layernorm.hip", "frontend.hip", "xattn.hip", "argmax.hip", "wenc_runtime.cpp"]
 
 # Per-source flags.  Attention runs softmax VALU work on the MFMA results:
 # keeping them in ordinary VGPRs avoids copies between AGPRs and VGPRs.

@@ -45,6 +45,14 @@ const char *xattn_check(int batch, int n_head, int n_q, int T);
 hipError_t launch_xattn(const uint16_t *q, const uint16_t *xk, const uint16_t *xv, uint16_t *out, float *part,
                         int batch, int n_head, int n_q, int T, hipStream_t s);
 
+// Greedy argmax per row (argmax.hip): logits fp32 [rows][ld], out int32
+// [rows]; part: workspace of rows * argmax_chunks(n_vocab) keys (unused when
+// that is one chunk per row).
+int argmax_chunks(int n_vocab);
+const char *argmax_check(int rows, int n_vocab, int64_t ld);
+hipError_t launch_argmax(const float *logits, int rows, int n_vocab, int64_t ld, uint64_t *part, int32_t *out,
+                         hipStream_t s);
+
 // y fp16 [n] = x fp32 [n] rounded to nearest even; n % 4 == 0, 16-byte aligned.
 hipError_t launch_to_f16(const float *x, uint16_t *y, int64_t n, hipStream_t s);
 

@@ -749,6 +749,31 @@ int wenc_cross_attend(wenc_t *h, const void *q, const void *xk, const void *xv, 
     return WENC_OK;
 }
 
+int wenc_argmax(wenc_t *h, const float *logits, int32_t rows, int32_t n_vocab, int64_t ld, int32_t *out,
+                void *stream) {
+    if (!h) return fail(nullptr, WENC_EINVAL, "wenc_argmax: handle is NULL");
+    const wenc_config &c = h->cfg;
+    if (const char *m = wk::argmax_check(rows, n_vocab, ld)) return fail(&h->err, WENC_EINVAL, "wenc_argmax: %s", m);
+    if (rows == 0) return WENC_OK;
+    if (!logits || !out) return fail(&h->err, WENC_EINVAL, "wenc_argmax: null pointer");
+    if ((reinterpret_cast<uintptr_t>(logits) | reinterpret_cast<uintptr_t>(out)) & 3)
+        return fail(&h->err, WENC_EINVAL, "wenc_argmax: logits and out must be 4-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // the chunk keys live in the fp16 LayerNorm-output region of the scratch
+    const size_t room = size_t(2) * c.max_batch * c.n_ctx * c.d_model;
+    const size_t per = size_t(wk::argmax_chunks(n_vocab)) * sizeof(uint64_t);
+    if (per > room) return fail(&h->err, WENC_EINVAL, "wenc_argmax: the scratch cannot hold one row's chunk keys");
+    const int cap = int(std::max<size_t>(1, std::min<size_t>(room / per, size_t(rows))));
+    uint64_t *part = h->S<uint64_t>(h->sl.xn);
+    for (int r0 = 0; r0 < rows; r0 += cap) {
+        const int nr = rows - r0 < cap ? rows - r0 : cap;
+        WENC_TRY(h->site(WENC_SITE_ARGMAX, st, [&] {
+            return wk::launch_argmax(logits + size_t(r0) * size_t(ld), nr, n_vocab, ld, part, out + r0, st);
+        }));
+    }
+    return WENC_OK;
+}
+
 int wenc_log_mel(wenc_t *h, const float *audio, int32_t batch, float *mel, void *stream) {
     if (!h) return fail(nullptr, WENC_EINVAL, "wenc_log_mel: handle is NULL");
     const wenc_config &c = h->cfg;

@@ -26,7 +26,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 WENC_OK, WENC_EINVAL, WENC_ENOMEM, WENC_ENODEV, WENC_ESTATE, WENC_EHIP = 0, -1, -2, -3, -4, -5
 WENC_TAP_C1, WENC_TAP_STEM, WENC_TAP_BLOCK = 0, 1, 2
 WENC_EPI_GELU_F16, WENC_EPI_CONV2, WENC_EPI_RESID, WENC_EPI_QKV, WENC_EPI_KV = 0, 1, 2, 3, 4
-SITES = ("ingest", "conv1", "conv2", "ln1", "qkv", "attn", "oproj", "ln2", "fc1", "fc2", "lnf", "xcvt", "xkv", "mel", "xatt")
+SITES = ("ingest", "conv1", "conv2", "ln1", "qkv", "attn", "oproj", "ln2", "fc1", "fc2", "lnf", "xcvt", "xkv", "mel", "xatt", "amax")
 N_SITES = len(SITES)
 
 
@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
     L.wenc_prepare_cross.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     L.wenc_cross_attend.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
     L.wenc_cross_attend.restype = ctypes.c_int
+    L.wenc_argmax.argtypes = [vp, vp, i32, i32, ctypes.c_int64, vp, vp]
+    L.wenc_argmax.restype = ctypes.c_int
     L.wenc_prepare_cross.restype = ctypes.c_int
     L.wenc_log_mel.argtypes = [vp, vp, i32, vp, vp]
     L.wenc_log_mel.restype = ctypes.c_int
@@ -193,6 +195,10 @@ def wenc_prepare_cross(h, memory: torch.Tensor, batch: int, n_ctx: int, xk: torc
 def wenc_cross_attend(h, q: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, batch: int, n_q: int, n_ctx: int,
                       out: torch.Tensor, stream=None) -> None:
     _check(lib().wenc_cross_attend(h, _ptr(q), _ptr(xk), _ptr(xv), batch, n_q, n_ctx, _ptr(out), _stream(stream)), h)
+
+
+def wenc_argmax(h, logits: torch.Tensor, rows: int, n_vocab: int, ld: int, out: torch.Tensor, stream=None) -> None:
+    _check(lib().wenc_argmax(h, _ptr(logits), rows, n_vocab, ld, _ptr(out), _stream(stream)), h)
 
 
 def wenc_forward_tap(h, mel: torch.Tensor, batch: int, tap: int, dst: torch.Tensor, stream=None) -> None:
@@ -316,6 +322,20 @@ class Encoder:
         if out is None:
             out = torch.empty_like(q)
         wenc_cross_attend(self.h, q, xk, xv, q.shape[0], q.shape[1], xk.shape[1], out, stream)
+        return out
+
+    def argmax(self, logits: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+        """Greedy token choice: per row of logits [rows, n_vocab] fp32 (rows
+        may be strided), the index of the largest value: int32 [rows]."""
+        if not (logits.is_cuda and logits.dtype == torch.float32 and logits.dim() == 2
+                and logits.stride(1) == 1 and logits.stride(0) >= logits.shape[1]):
+            raise ValueError("logits must be an fp32 device tensor [rows, n_vocab] with unit column stride")
+        rows, n = logits.shape
+        if out is None:
+            out = torch.empty((rows,), dtype=torch.int32, device=logits.device)
+        elif not (out.is_cuda and out.dtype == torch.int32 and out.is_contiguous() and out.shape == (rows,)):
+            raise ValueError("out must be a contiguous int32 device tensor [rows]")
+        wenc_argmax(self.h, logits, rows, n, logits.stride(0), out, stream)
         return out
 
     def tap(self, mel: torch.Tensor, tap: int, stream=None) -> torch.Tensor:
