@@ -136,6 +136,31 @@ def test_gemm_gelu_f16(M, N, K):
     np.testing.assert_allclose(host(C)[rows].astype(np.float64), ref, rtol=1e-3, atol=1e-4)
 
 
+def test_gemm_gelu_over_its_whole_range():
+    """The GELU epilogue at pre-activations spanning [-16, 16] densely
+    (every fp16 value there, plus per-column fp32 bias offsets), including the
+    far tails where the normal-tail term underflows: each fp16 output within
+    one fp16 ulp (or 1e-6) of the exact GELU of the fp32 pre-activation."""
+    top = int(np.float16(16.0).view(np.uint16))  # bit patterns 0 .. top are +0 .. 16; with the sign bit, -0 .. -16
+    z16 = np.arange(0, top + 1, dtype=np.uint16)
+    z16 = np.concatenate([z16, z16 | np.uint16(0x8000)]).view(np.float16)
+    M, N, K = len(z16), 64, 8
+    say(f"gemm gelu range M={M}")
+    A = np.zeros((M, K), np.float16)
+    A[:, 0] = z16
+    W = np.zeros((N, K), np.float16)
+    W[:, 0] = 1.0
+    b = (np.arange(N, dtype=np.float32) - 32) * np.float32(1e-3)
+    C = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    _gemm(f16_dev(A), f16_dev(W), dev(b), wenc.WENC_EPI_GELU_F16, M, N, K, C=C)
+    pre = z16.astype(np.float32)[:, None] + b[None, :]  # the fp32 accumulator: one exact product plus the bias
+    ref = oracle.gelu(pre.astype(np.float64))
+    got = host(C).astype(np.float64)
+    ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+    bad = np.abs(got - ref) > np.maximum(ulp, 1e-6)
+    assert not bad.any(), (int(bad.sum()), pre[bad][:5], got[bad][:5], ref[bad][:5])
+
+
 def test_gemm_empty_m():
     z = torch.zeros(64, dtype=torch.float16, device=DEV)
     _gemm(z, z, torch.zeros(8, device=DEV), wenc.WENC_EPI_RESID, 0, 8, 8, C=z)

@@ -33,30 +33,24 @@ __device__ __forceinline__ uint32_t divu(uint32_t n, const DivU &v) {
 }
 
 // Exact GELU, the error-function form: gelu(z) = z Phi(z), Phi(z) =
-// 0.5 (1 + erf(z / sqrt 2)).  erf comes from Abramowitz & Stegun, Handbook of
-// Mathematical Functions (1964), formula 7.1.28 (|error| <= 3e-7): for x >= 0,
-//   1 - erf(x) = (1 + a1 x + a2 x^2 + a3 x^3 + a4 x^4 + a5 x^5 + a6 x^6)^-16.
-// With x = |z| / sqrt 2 and r = 0.5 (1 - erf(x)), Phi(z) = 1 - r for z >= 0
-// and r for z < 0, so in both cases gelu(z) = max(z, 0) - |z| r.  The
-// coefficients below are a_k 2^(-k/2) (the 1/sqrt 2 folded in) times
-// 2^(1/16) (so the 16th power carries the 0.5), leaving six FMAs, four
-// squarings, one reciprocal and one FMA.  In fp32 the result is within
-// 7.1e-7 of the exact GELU everywhere (checked on a dense grid over
-// [-12, 12]); for large |z| the 16th power overflows to +inf, r to 0 and the
-// result to max(z, 0), as it should.
+// 0.5 (1 + erf(z / sqrt 2)).  With Q(u) = Phi(-u), the upper normal tail,
+// Phi(z) = 1 - Q(|z|) for z >= 0 and Q(|z|) for z < 0, so in both cases
+// gelu(z) = max(z, 0) - |z| Q(|z|).  Q is evaluated as 2^p(u), p a degree-5
+// polynomial fitted to log2 Q on [0, 6] so as to minimise the largest error
+// of u Q(u) (gelu_tail_fit.py beside this file derives the coefficients and
+// checks them): five FMAs, one exp2, one max and one FMA.  In fp32 the result
+// is within 4.7e-7 of the exact GELU everywhere (dense grid over [-12, 12]);
+// p decreases for all u >= 0, so past the fitted range the tail term keeps
+// shrinking (< 5e-9 beyond u = 6) and exp2 underflows to 0 for large |z|,
+// leaving max(z, 0).
 __device__ __forceinline__ float gelu_erf(float z) {
     const float u = fabsf(z);
-    float q = fmaf(5.621299806e-06f, u, 5.105520904e-05f);
-    q = fmaf(q, u, 3.968613601e-05f);
-    q = fmaf(q, u, 3.422739217e-03f);
-    q = fmaf(q, u, 2.207699791e-02f);
-    q = fmaf(q, u, 5.207516253e-02f);
-    q = fmaf(q, u, 1.044273734e+00f);
-    q *= q;
-    q *= q;
-    q *= q;
-    q *= q;
-    const float r = __builtin_amdgcn_rcpf(q);
+    float p = fmaf(-4.733079986e-4f, u, 7.084549870e-3f);
+    p = fmaf(p, u, -5.182737112e-2f);
+    p = fmaf(p, u, -4.599924386e-1f);
+    p = fmaf(p, u, -1.150787830e+0f);
+    p = fmaf(p, u, -1.000037670e+0f);
+    const float r = __builtin_amdgcn_exp2f(p);
     // max(z, 0) as one instruction: fmaxf would first quiet a signalling NaN
     // with an extra max.  A NaN z still yields NaN through -u.
     float pos;
