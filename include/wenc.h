@@ -275,6 +275,15 @@ int wenc_argmax(wenc_t *h, const float *logits, int32_t rows, int32_t n_vocab, i
  * values out of range. */
 int wenc_k_gemm_mode(int32_t tile, int32_t split);
 
+/* Test-only, host logic (no device work): the tile plan wenc_k_gemm would use
+ * for M output rows (after the QKV epilogue's padding to 16 keys per item)
+ * and N columns on `cus` compute units, with tile and split as in
+ * wenc_k_gemm_mode (tile -1 = automatic, ignoring the environment).  Returns
+ * 0 = all 128 x 128 tiles, 1 = all 256 x 256 tiles, 2 = 256 x 256 tiles for
+ * rows [0, *big_rows) and 128 x 128 for the rest; *big_rows is M for 1 and
+ * 0 for 0.  WENC_EINVAL for values out of range. */
+int wenc_k_gemm_plan(int32_t M, int32_t N, int32_t cus, int32_t tile, int32_t split, int32_t *big_rows);
+
 /* Non-causal attention per (batch, head) (kernels.nu, wk_attn with causal 0):
  *   ao[b][t][h*64 + e] = sum_u softmax_u(q[b][h][t] . k[b][h][u]) * v[b][h][u][e]
  * with q ALREADY scaled by log2(e)/sqrt(64) (the softmax is taken in base 2),

@@ -646,13 +646,27 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag) {
         const char *f = std::getenv("WENC_GEMM_SPLIT");
         g_split = f ? std::atoi(f) : 1;
     }
-    if (g_tile_override == 1) return launch_tagged<256, 256, 128, 64, 8>(p, a.epilogue, tag, s);
-    if (g_tile_override == 0) return launch_tagged<128, 128, 64, 64, 4>(p, a.epilogue, tag, s);
+    const GemmPlan plan = gemm_plan(p.M, p.N, cu_count(), g_tile_override == 0 || g_tile_override == 1 ? g_tile_override : -1,
+                                    g_split);
+    if (plan.kind == GEMM_PLAN_SMALL) return launch_tagged<128, 128, 64, 64, 4>(p, a.epilogue, tag, s);
+    if (plan.kind == GEMM_PLAN_BIG) return launch_tagged<256, 256, 128, 64, 8>(p, a.epilogue, tag, s);
+    GemmP big = p;
+    big.M = plan.big_rows;
+    const hipError_t e = launch_tagged<256, 256, 128, 64, 8>(big, a.epilogue, tag, s);
+    if (e != hipSuccess) return e;
+    GemmP tail = p;
+    tail.m_begin = plan.big_rows;
+    return launch_tagged<128, 128, 64, 64, 4>(tail, a.epilogue, tag, s);
+}
+
+GemmPlan gemm_plan(int M, int N, long cus, int tile, int split) {
+    if (tile == 1) return {GEMM_PLAN_BIG, M};
+    if (tile == 0) return {GEMM_PLAN_SMALL, 0};
     // 256 x 256 tiles when they fill the CUs nearly twice over (measured: on
     // 24000 x 768 x {768, 3072}, 282 such tiles, the 128 x 128 tiles at two
     // workgroups per CU are 10-20% faster).
-    const long tn_big = (p.N + 255) / 256, tm_big = (p.M + 255) / 256;
-    if (tm_big * tn_big < 448) return launch_tagged<128, 128, 64, 64, 4>(p, a.epilogue, tag, s);
+    const long tn_big = (N + 255) / 256, tm_big = (long(M) + 255) / 256;
+    if (tm_big * tn_big < 448) return {GEMM_PLAN_SMALL, 0};
     // The 256 x 256 kernel runs one tile per CU at a time, so a tile count
     // just past a multiple of the CU count leaves most CUs idle in the last
     // round.  Then the last tile rows go to the 128 x 128 kernel instead (two
@@ -660,12 +674,11 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag) {
     // kernels sum each output over k in the same order, so the split changes
     // no result bit.  R = the number of 256-row tile rows kept big.
     long best_r = tm_big;
-    if (g_split) {
-        const long cus = cu_count();
+    if (split) {
         auto rounds = [](long n, long per) { return double((n + per - 1) / per); };
         double best = rounds(tm_big * tn_big, cus);
         for (long r = tm_big - 1; r >= 1 && r >= tm_big - 64; --r) {
-            const long small = ((p.M - 256 * r + 127) / 128) * ((p.N + 127) / 128);
+            const long small = ((M - 256 * r + 127) / 128) * ((N + 127) / 128);
             const double cost = rounds(r * tn_big, cus) + 0.6 * rounds(small, 2 * cus);
             if (cost < best - 0.05) {
                 best = cost;
@@ -673,14 +686,8 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag) {
             }
         }
     }
-    if (best_r == tm_big) return launch_tagged<256, 256, 128, 64, 8>(p, a.epilogue, tag, s);
-    GemmP big = p;
-    big.M = int(256 * best_r);
-    const hipError_t e = launch_tagged<256, 256, 128, 64, 8>(big, a.epilogue, tag, s);
-    if (e != hipSuccess) return e;
-    GemmP tail = p;
-    tail.m_begin = int(256 * best_r);
-    return launch_tagged<128, 128, 64, 64, 4>(tail, a.epilogue, tag, s);
+    if (best_r == tm_big) return {GEMM_PLAN_BIG, M};
+    return {GEMM_PLAN_SPLIT, int(256 * best_r)};
 }
 
 }  // namespace wk
