@@ -28,8 +28,9 @@ namespace {
 constexpr int NFFT = 400;
 constexpr int HOP = 160;
 constexpr int NBIN = NFFT / 2 + 1;  // 201
-constexpr int KT = 7;               // frequency tiles of 32 (224 >= 201)
+constexpr int KT = 7;               // frequency tiles of 32
 constexpr int KPAD = KT * 32;
+static_assert(KPAD >= NBIN, "the frequency tiles cover every bin");
 constexpr int TF = 32;              // frames per workgroup (one wave)
 constexpr int SPAN = HOP * (TF - 1) + NFFT;  // samples the 32 frames read: 5360
 constexpr int NSEG = (SPAN + HOP - 1) / HOP;  // 160-sample segments: 34

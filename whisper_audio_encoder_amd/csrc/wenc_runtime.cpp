@@ -479,7 +479,7 @@ int wenc_create(const wenc_config *cfg, wenc_t **out) {
         if (ea != hipSuccess) {
             (void)hipGetLastError();
             size_t fr = 0, tot = 0;
-            hipMemGetInfo(&fr, &tot);
+            (void)hipMemGetInfo(&fr, &tot);  // best effort: the message reports 0 if it fails
             *p = nullptr;
             return fail(nullptr, WENC_ENOMEM, "wenc_create: cannot allocate %zu bytes of %s (device has %zu free of %zu)",
                         bytes, what, fr, tot);
@@ -512,9 +512,9 @@ int wenc_create(const wenc_config *cfg, wenc_t **out) {
         }
     }
     if (rc != WENC_OK) {
-        if (h->warena) hipFree(h->warena);
-        if (h->sarena) hipFree(h->sarena);
-        if (h->farena) hipFree(h->farena);
+        if (h->warena) (void)hipFree(h->warena);
+        if (h->sarena) (void)hipFree(h->sarena);
+        if (h->farena) (void)hipFree(h->farena);
         delete h;
         return rc;
     }
@@ -651,8 +651,10 @@ int wenc_load_cross(wenc_t *h, int32_t n_dec_layer, const void *blob, size_t nby
     hipError_t e = hipSetDevice(h->device);
     if (e != hipSuccess) return fail(&h->err, WENC_EHIP, "wenc_load_cross: hipSetDevice: %s", hipGetErrorString(e));
     if (h->xarena) {
-        hipDeviceSynchronize();  // no enqueued work may still read the old weights
-        hipFree(h->xarena);
+        e = hipDeviceSynchronize();  // no enqueued work may still read the old weights
+        if (e == hipSuccess) e = hipFree(h->xarena);
+        if (e != hipSuccess)
+            return fail(&h->err, WENC_EHIP, "wenc_load_cross: releasing the previous weights: %s", hipGetErrorString(e));
         h->xarena = nullptr;
         h->n_dec = 0;
     }
@@ -660,7 +662,7 @@ int wenc_load_cross(wenc_t *h, int32_t n_dec_layer, const void *blob, size_t nby
     if (e != hipSuccess) {
         (void)hipGetLastError();
         size_t fr = 0, tot = 0;
-        hipMemGetInfo(&fr, &tot);
+        (void)hipMemGetInfo(&fr, &tot);  // best effort: the message reports 0 if it fails
         h->xarena = nullptr;
         return fail(&h->err, WENC_ENOMEM, "wenc_load_cross: cannot allocate %zu bytes (device has %zu free of %zu)",
                     host.size(), fr, tot);
@@ -799,16 +801,17 @@ int wenc_log_mel(wenc_t *h, const float *audio, int32_t batch, float *mel, void 
 
 void wenc_destroy(wenc_t *h) {
     if (!h) return;
-    hipDeviceSynchronize();
+    // teardown: errors cannot be acted on here, every release is attempted
+    (void)hipDeviceSynchronize();
     for (auto &r : h->prof_pending) {
-        hipEventDestroy(r.e0);
-        hipEventDestroy(r.e1);
+        (void)hipEventDestroy(r.e0);
+        (void)hipEventDestroy(r.e1);
     }
-    for (auto e : h->event_pool) hipEventDestroy(e);
-    if (h->warena) hipFree(h->warena);
-    if (h->sarena) hipFree(h->sarena);
-    if (h->xarena) hipFree(h->xarena);
-    if (h->farena) hipFree(h->farena);
+    for (auto e : h->event_pool) (void)hipEventDestroy(e);
+    if (h->warena) (void)hipFree(h->warena);
+    if (h->sarena) (void)hipFree(h->sarena);
+    if (h->xarena) (void)hipFree(h->xarena);
+    if (h->farena) (void)hipFree(h->farena);
     delete h;
 }
 
