@@ -135,5 +135,16 @@ def test_cross_errors():
         wenc.wenc_prepare_cross(enc.h, mem, 1, cfg.n_ctx, xk, xv)
         assert not host(xk).any()
         assert np.array_equal(host(xv)[0, 0], np.broadcast_to(cross["d0.x_bv"], (cfg.n_ctx, cfg.d_model)))
+        # reloading replaces the previous weights (a different depth and values)
+        cross2 = synth.make_cross_params(cfg, 2)
+        cross2 = {k: (v + np.float16(0.5)).astype(np.float16) for k, v in cross2.items()}
+        enc.load_cross(synth.pack_cross_blob(cfg, cross2, 2), 2)
+        xk2 = torch.empty((2, 1, cfg.n_ctx, cfg.d_model), dtype=torch.float16, device=DEV)
+        xv2 = torch.empty_like(xk2)
+        wenc.wenc_prepare_cross(enc.h, mem, 1, cfg.n_ctx, xk2, xv2)
+        for layer in range(2):
+            assert not host(xk2[layer]).any()
+            assert np.array_equal(host(xv2)[layer, 0],
+                                  np.broadcast_to(cross2[f"d{layer}.x_bv"], (cfg.n_ctx, cfg.d_model)))
     finally:
         enc.close()
