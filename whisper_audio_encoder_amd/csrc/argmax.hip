@@ -2,9 +2,9 @@
 //
 // Greedy decoding takes, per sequence and step, the index of the largest of
 // the vocabulary's logits (51865 for Whisper); the whisper README
-// ("Performance and memory") reports that copying all of them to the host
-// to search there cost more than the step's attention, and that the remedy
-// is to reduce on the device and return one integer.  Per row r:
+// ("Performance and memory") names fetching all of them to the host for
+// that search as one of the two costs it removed from a decode step, by
+// reducing on the device and returning one integer.  Per row r:
 //   out[r] = min { i : logits[r][i] = max_j logits[r][j] }
 // where a NaN counts as larger than every number (the first NaN wins) and
 // -0.0 equals +0.0.
