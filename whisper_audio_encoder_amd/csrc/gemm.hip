@@ -24,7 +24,8 @@
 //
 // Workgroup ids are remapped so that each XCD (ids are dealt round-robin
 // over the 8 XCDs) receives a contiguous run of tiles, ordered in groups of
-// 8 tile rows, so tiles sharing A rows or W rows share that XCD's L2.
+// a few tile rows (tile_coords), so tiles sharing A rows or W rows share
+// that XCD's L2.
 #include <cstdlib>
 
 #include "common.h"
@@ -65,11 +66,17 @@ struct GemmP {
     int tiles_m, tiles_n;
 };
 
+// Group height GM: a run of consecutive tiles covers GM tile rows across all
+// tile columns, and an XCD runs about 32 consecutive tiles at once, so GM x
+// tiles_n near 32 lets one round read each A row panel into that XCD's L2
+// for all its column tiles.  Measured on the encoder's projections (d 1280):
+// 6 for five columns (fc2, out_proj, conv2: fc2 -3.5%), 4 for 15 to 20
+// (q|k|v, fc1: -1 to -2%), 8 otherwise (unchanged at d 768).
 __device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int tiles_n, int &tm, int &tn) {
     const int per = nwg >> 3, rem = nwg & 7;
     const int xcd = bid & 7, idx = bid >> 3;
     const int lid = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-    constexpr int GM = 8;
+    const int GM = tiles_n <= 5 ? 6 : (tiles_n >= 15 ? 4 : 8);
     const int group_size = GM * tiles_n;
     const int g = lid / group_size;
     const int first_m = g * GM;
