@@ -115,6 +115,32 @@ def test_poisoned_scratch_gives_same_output(monkeypatch):
     assert np.array_equal(out, host(encoder(name).forward(dev(mel))))
 
 
+def test_non_finite_input_propagates_within_its_window():
+    """A NaN or an infinity in one window's mel is not sanitised: that
+    window's whole memory becomes NaN (every position attends to the
+    poisoned keys), as in the oracle, and the other windows' outputs keep
+    every bit."""
+    name = "c2"
+    cfg, mel, params, _ = inputs(name)
+    say("non-finite mel c2")
+    enc = encoder(name)
+    clean = host(enc.forward(dev(mel)))
+    bad = mel.copy()
+    bad[2, 1234, 17] = np.nan
+    bad[5, 2999, 0] = np.inf
+    out = host(enc.forward(dev(bad)))
+    for b in (2, 5):
+        assert np.isnan(out[b]).all(), b
+    for b in (0, 1, 3, 4, 6, 7):
+        assert np.array_equal(out[b], clean[b]), b
+    small = CONFIGS["c0"]
+    m0, p0 = synth.make_inputs(small)
+    m0 = m0.copy()
+    m0[0, 1234, 17] = np.nan
+    ref = oracle.encode(m0[0], p0, small.n_layer, small.n_head)
+    assert np.isnan(ref).all()
+
+
 def test_no_final_ln_and_zero_layers():
     base = CONFIGS["c0"]
     rng_cfg = base.with_(n_layer=0, final_ln=0, name="c0-l0")
