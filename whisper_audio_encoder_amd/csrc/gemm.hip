@@ -16,8 +16,9 @@
 // lies beyond the descriptor's range and reads as zero, which pads the M, N
 // and K tails without branches.  Within LDS, 16-byte chunks are XOR-swizzled
 // by row so that fragment reads are free of bank conflicts; the direct loads
-// produce that layout by choosing which global chunk each lane fetches.  LDS is double
-// buffered: step k+1 is in flight while step k's MFMAs run, with one barrier
+// produce that layout by choosing which global chunk each lane fetches.  The
+// A part of a step has three LDS buffers and the W part two: A of step k+2
+// and W of step k+1 are in flight while step k's MFMAs run, with one barrier
 // per step.  The MFMA takes W as its A operand and A^T as its B operand, so
 // each lane ends up owning one output row and runs of 4 consecutive output
 // columns, which the epilogues store as 8- or 16-byte vectors.
@@ -202,8 +203,10 @@ gemm_kernel(const GemmP p) {
     constexpr int BG = BN / 8 / LW;
     static_assert(AG >= 1 && BG >= 1, "each loading wave moves at least one group");
     constexpr int STAGE = (BM + BN) * BK;  // halves per LDS stage
-    __shared__ __attribute__((aligned(1024))) f16 smem0[STAGE];
-    __shared__ __attribute__((aligned(1024))) f16 smem1[STAGE];
+    constexpr int ASZ = BM * BK;           // halves of the A part of a stage
+    __shared__ __attribute__((aligned(1024))) f16 smem0[STAGE];  // A buffer 0 | W buffer 0
+    __shared__ __attribute__((aligned(1024))) f16 smem1[STAGE];  // A buffer 1 | W buffer 1
+    __shared__ __attribute__((aligned(1024))) f16 smemA2[ASZ];   // A buffer 2
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS addresses stay scalar
@@ -239,28 +242,37 @@ gemm_kernel(const GemmP p) {
     const i32x4 ra = make_rsrc(p.A + a0);
     const i32x4 rb = make_rsrc(p.W + int64_t(n0) * p.ldw);
 
-    const uint32_t lds0 = lds_addr(smem0), lds1 = lds_addr(smem1);
-    // Direct loads of K step kt into the stage at LDS byte address st.  Steps
-    // that lie wholly inside K (every step when K % 64 == 0) skip the K-tail
-    // test.
-    auto issue = [&](int kt, uint32_t st) __attribute__((always_inline)) {
+    const uint32_t lds0 = lds_addr(smem0), lds1 = lds_addr(smem1), lds2 = lds_addr(smemA2);
+    const uint32_t la0 = lds0, la1 = lds1, la2 = lds2;                 // A buffers
+    const uint32_t lw0 = lds0 + ASZ * 2, lw1 = lds1 + ASZ * 2;         // W buffers
+    // Direct loads of K step kt: the A part into the A buffer at LDS byte
+    // address st, the W part into the W buffer at st.  Steps that lie wholly
+    // inside K (every step when K % 64 == 0) skip the K-tail test.
+    auto issueA = [&](int kt, uint32_t st) __attribute__((always_inline)) {
         if (wave >= LW) return;
         const uint32_t kb = uint32_t(kt) * (BK * 2);
         if ((kt + 1) * BK <= p.K) {
 #pragma unroll
             for (int g = 0; g < AG; ++g) load_lds16(ra, st + (lw * AG + g) * 8 * BK * 2, a_off[g] + kb);
-#pragma unroll
-            for (int g = 0; g < BG; ++g) load_lds16(rb, st + (BM + (lw * BG + g) * 8) * BK * 2, b_off[g] + kb);
         } else {
 #pragma unroll
             for (int g = 0; g < AG; ++g) {
                 const uint32_t kflag = (kt * BK + int(a_ch[g]) * 8 < p.K) ? 0u : OOB;
                 load_lds16(ra, st + (lw * AG + g) * 8 * BK * 2, (a_off[g] | kflag) + kb);
             }
+        }
+    };
+    auto issueW = [&](int kt, uint32_t st) __attribute__((always_inline)) {
+        if (wave >= LW) return;
+        const uint32_t kb = uint32_t(kt) * (BK * 2);
+        if ((kt + 1) * BK <= p.K) {
+#pragma unroll
+            for (int g = 0; g < BG; ++g) load_lds16(rb, st + (lw * BG + g) * 8 * BK * 2, b_off[g] + kb);
+        } else {
 #pragma unroll
             for (int g = 0; g < BG; ++g) {
                 const uint32_t kflag = (kt * BK + int(b_ch[g]) * 8 < p.K) ? 0u : OOB;
-                load_lds16(rb, st + (BM + (lw * BG + g) * 8) * BK * 2, (b_off[g] | kflag) + kb);
+                load_lds16(rb, st + (lw * BG + g) * 8 * BK * 2, (b_off[g] | kflag) + kb);
             }
         }
     };
@@ -294,17 +306,15 @@ gemm_kernel(const GemmP p) {
     // with one A-side set live.  The barrier that publishes step kt+1 sits
     // between the two slices of step kt: slice 1's fragments are already in
     // registers, so its MFMAs overlap the barrier and the reads of step
-    // kt+1's slice 0, and the direct loads of step kt+2 go into the buffer
-    // step kt has just released.  Steps alternate between the two LDS
-    // buffers in a loop unrolled by two, so every LDS access names its buffer
-    // statically and the compiler can tell a transfer into one buffer from
-    // reads of the other.  (The last step's slice 1 reads the idle buffer;
-    // those fragments are not used.)
+    // kt+1's slice 0, and the direct loads of W for step kt+2 and of A for
+    // step kt+3 go into the buffers step kt has just released.  (The last
+    // step's slice 1 reads idle buffers; those fragments are not used.)
     const int nk = (p.K + BK - 1) / BK;
     f16x8 af[TM], bf0[TN], bf1[TN];
-    auto slice = [&](const f16x8 (&bfc)[TN], f16x8 (&bfn)[TN], const f16 *src, int kk) __attribute__((always_inline)) {
-        const f16 *as = src + (wm * WM + frow) * BK;
-        const f16 *bs = src + BM * BK + (wn * WN + frow) * BK;
+    auto slice = [&](const f16x8 (&bfc)[TN], f16x8 (&bfn)[TN], const f16 *asrc, const f16 *wsrc, int kk)
+                     __attribute__((always_inline)) {
+        const f16 *as = asrc + (wm * WM + frow) * BK;
+        const f16 *bs = wsrc + (wn * WN + frow) * BK;
         const int ch = ((kk * 4 + (lane >> 4)) ^ fsw) << 3;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -325,33 +335,64 @@ gemm_kernel(const GemmP p) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
     };
-    auto step = [&](int kt, f16 *cur, f16 *nxt, uint32_t cur_lds) __attribute__((always_inline)) {
-        slice(bf0, bf1, cur, 1);
+    // A tiles rotate through three buffers and W tiles through two: at the
+    // barrier of step kt the buffers of tile kt are free, and they receive
+    // A of step kt + 3 and W of step kt + 2 (issued W first).  So an A
+    // transfer has two steps to land and a W transfer one.  The wait before
+    // the barrier needs tile kt + 1: its A went out a step before the W, and
+    // each wave's transfers complete in issue order, so only the AG
+    // transfers of A for step kt + 2 may still be outstanding.
+    auto step = [&](int kt, const f16 *a_cur, const f16 *w_cur, const f16 *a_nxt, const f16 *w_nxt, uint32_t a_cur_lds,
+                    uint32_t w_cur_lds) __attribute__((always_inline)) {
+        slice(bf0, bf1, a_cur, w_cur, 1);
         __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        if (kt + 2 < nk)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(AG) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
-        if (kt + 2 < nk) issue(kt + 2, cur_lds);
+        if (kt + 2 < nk) issueW(kt + 2, w_cur_lds);
+        if (kt + 3 < nk) issueA(kt + 3, a_cur_lds);
         __builtin_amdgcn_sched_barrier(0);
-        slice(bf1, bf0, nxt, 0);
+        slice(bf1, bf0, a_nxt, w_nxt, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
-    issue(0, lds0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const f16 *A0 = smem0, *A1 = smem1, *A2 = smemA2, *W0 = smem0 + ASZ, *W1 = smem1 + ASZ;
+    issueW(0, lw0);
+    issueA(0, la0);
+    if (nk > 1) {
+        issueA(1, la1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(AG) : "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
-    if (nk > 1) issue(1, lds1);
+    if (nk > 1) issueW(1, lw1);
+    if (nk > 2) issueA(2, la2);
     {
-        const f16 *as = smem0 + (wm * WM + frow) * BK;
-        const f16 *bs = smem0 + BM * BK + (wn * WN + frow) * BK;
+        const f16 *as = A0 + (wm * WM + frow) * BK;
+        const f16 *bs = W0 + (wn * WN + frow) * BK;
         const int ch = ((lane >> 4) ^ fsw) << 3;
 #pragma unroll
         for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const f16x8 *>(as + i * 16 * BK + ch);
 #pragma unroll
         for (int j = 0; j < TN; ++j) bf0[j] = *reinterpret_cast<const f16x8 *>(bs + j * 16 * BK + ch);
     }
+    // unrolled by six (A period 3, W period 2) so every LDS access names its
+    // buffer statically
 #pragma unroll 1
-    for (int kt = 0; kt < nk; kt += 2) {
-        step(kt, smem0, smem1, lds0);
-        if (kt + 1 < nk) step(kt + 1, smem1, smem0, lds1);
+    for (int kt = 0; kt < nk; kt += 6) {
+        step(kt, A0, W0, A1, W1, la0, lw0);
+        if (kt + 1 >= nk) break;
+        step(kt + 1, A1, W1, A2, W0, la1, lw1);
+        if (kt + 2 >= nk) break;
+        step(kt + 2, A2, W0, A0, W1, la2, lw0);
+        if (kt + 3 >= nk) break;
+        step(kt + 3, A0, W1, A1, W0, la0, lw1);
+        if (kt + 4 >= nk) break;
+        step(kt + 4, A1, W0, A2, W1, la1, lw0);
+        if (kt + 5 >= nk) break;
+        step(kt + 5, A2, W1, A0, W0, la2, lw1);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
