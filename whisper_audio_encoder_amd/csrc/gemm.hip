@@ -11,15 +11,16 @@
 // is exactly the operand layout v_mfma_f32_16x16x32_f16 reads per lane.
 //
 // Structure (details at each step below).  A workgroup of NW wave64s owns a
-// BM x BN output tile and walks K in steps of 64 (two MFMA k slices of 32).  Each step is moved from global memory straight into LDS
-// by buffer_load ... lds (no VGPR staging); a buffer offset with bit 31 set
+// BM x BN output tile and walks K in steps of 64 (two MFMA k slices of 32).
+// Each step is moved from global memory straight into LDS by
+// buffer_load ... lds (no VGPR staging); a buffer offset with bit 31 set
 // lies beyond the descriptor's range and reads as zero, which pads the M, N
 // and K tails without branches.  Within LDS, 16-byte chunks are XOR-swizzled
 // by row so that fragment reads are free of bank conflicts; the direct loads
 // produce that layout by choosing which global chunk each lane fetches.  The
-// A part of a step has three LDS buffers and the W part two: A of step k+2
-// and W of step k+1 are in flight while step k's MFMAs run, with one barrier
-// per step.  The MFMA takes W as its A operand and A^T as its B operand, so
+// A part of a step has three LDS buffers and the W part two, so A transfers
+// are issued three steps ahead of their use and W transfers two, with one
+// barrier per step.  The MFMA takes W as its A operand and A^T as its B operand, so
 // each lane ends up owning one output row and runs of 4 consecutive output
 // columns, which the epilogues store as 8- or 16-byte vectors.
 //
