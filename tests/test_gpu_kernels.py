@@ -229,6 +229,32 @@ def test_gemm_tile_configs_bitwise(epi):
         np.testing.assert_allclose(outs[0][rows].astype(np.float64), oracle.gelu(pre), rtol=1e-3, atol=1e-4)
 
 
+@pytest.mark.parametrize("K", [64, 128, 192, 256, 320, 384, 448, 704, 776])
+def test_gemm_every_pipeline_depth(K):
+    """The operand pipeline (A fetched three k-steps ahead through three LDS
+    buffers, W two through two, the loop unrolled by six) for 1, 2, 3, 4, 5,
+    6, 7 and 11 k-steps and 13 with a ragged K tail (776 = 12 x 64 + 8), so
+    the loop leaves at each of its six positions, on both tile sizes: the
+    fp64 sums within fp32 accumulation, and both tile sizes the same bits."""
+    M, N = 600, 640
+    say(f"gemm pipeline depth K={K}")
+    rng = np.random.default_rng(K)
+    A, W, b = _operands(rng, M, N, K)
+    Ad, Wd, bd = f16_dev(A), f16_dev(W), dev(b)
+    x0 = rng.standard_normal((M, N)).astype(np.float32)
+    outs = []
+    try:
+        for tile in (0, 1):
+            _gemm_mode(tile, 0)
+            C = dev(x0)
+            _gemm(Ad, Wd, bd, wenc.WENC_EPI_RESID, M, N, K, C=C)
+            outs.append(host(C))
+    finally:
+        _gemm_mode(-1, 1)
+    assert np.array_equal(outs[0], outs[1])
+    np.testing.assert_allclose(outs[0], x0 + _f64(A) @ _f64(W).T + b, rtol=1e-5, atol=1e-4)
+
+
 def test_gemm_qkv_tile_configs_bitwise():
     """The q|k|v scatter (rows padded to 16 keys per item) under every tile
     configuration, at the whisper-small shape (16 windows, 12 heads), which
