@@ -165,8 +165,19 @@ def time_graph(enc, mel_d, out, n_ctx, steps):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # per replay (median, minimum), like the eager per-call figures
+    per = []
+    for _ in range(max(steps // 2, 3)):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        g.replay()
+        c1.record(stream)
+        per.append((c0, c1))
+    torch.cuda.synchronize()
+    call_ms = sorted(c0.elapsed_time(c1) for c0, c1 in per)
     del g
-    return {"ms_per_step": ms, "value": mel_d.shape[0] / (ms * 1e-3)}
+    return {"ms_per_step": ms, "value": mel_d.shape[0] / (ms * 1e-3),
+            "per_call_ms": {"median": call_ms[len(call_ms) // 2], "min": call_ms[0], "calls": len(call_ms)}}
 
 
 def time_frontend(enc, model, B, steps):

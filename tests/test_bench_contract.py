@@ -77,3 +77,6 @@ def test_bench_json_line():
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
     assert d["cross_kv"]["n_dec_layer"] == 2 and d["cross_kv"]["decode_step_argmax"]["us_per_call"] > 0
     assert d["log_mel"]
+    for part in (d, d["graph_replay"]):
+        pc = part["per_call_ms"]
+        assert 0 < pc["min"] <= pc["median"] and pc["calls"] >= 3
