@@ -111,8 +111,15 @@ def cpu_baseline(cfg, mel, params, budget_s=30.0):
     t0 = time.perf_counter()
     oracle.encode(mel[0], params, cfg.n_layer, cfg.n_head, cfg.ln_eps, bool(cfg.final_ln))
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": 1.0 / dt, "unit": "windows/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one full window (batch item 0) of the same workload, fp64 numpy/OpenBLAS, {dt:.1f} s"}
+            "sample": f"one full window (batch item 0) of the same workload, fp64 numpy/OpenBLAS, {dt:.1f} s",
+            "cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
 PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix
