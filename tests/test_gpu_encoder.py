@@ -141,6 +141,21 @@ def test_non_finite_input_propagates_within_its_window():
     assert np.isnan(ref).all()
 
 
+def test_debug_sync_mode_gives_same_output(monkeypatch):
+    """WENC_DEBUG_SYNC=1 (a stream synchronise and error check after every
+    launch) changes no result bit and reports success."""
+    name = "c1"
+    cfg, mel, _, blob = inputs(name)
+    say("debug sync c1")
+    monkeypatch.setenv("WENC_DEBUG_SYNC", "1")
+    enc = wenc.Encoder(cfg, blob)
+    try:
+        out = host(enc.forward(dev(mel)))
+    finally:
+        enc.close()
+    assert np.array_equal(out, host(encoder(name).forward(dev(mel))))
+
+
 def test_no_final_ln_and_zero_layers():
     base = CONFIGS["c0"]
     rng_cfg = base.with_(n_layer=0, final_ln=0, name="c0-l0")
