@@ -33,11 +33,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 template <int NV, bool OUT32>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64)
 ln_kernel(const float *__restrict__ x, const float *__restrict__ g, const float *__restrict__ bta,
           void *__restrict__ y, int rows, int d, float eps) {
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int row = blockIdx.x;
     if (row >= rows) return;
     const int nv = d >> 2;
     const float4 *xr = reinterpret_cast<const float4 *>(x + int64_t(row) * d);
@@ -88,7 +88,8 @@ ln_kernel(const float *__restrict__ x, const float *__restrict__ g, const float 
 template <int NV>
 hipError_t ln_dispatch(const float *x, const float *g, const float *b, void *y, int rows, int d, float eps,
                        bool out_f32, hipStream_t s) {
-    const dim3 grid((rows + 3) / 4), block(256);
+    // one wave per workgroup (measured 1-3% faster than four rows per 256-lane workgroup)
+    const dim3 grid(rows), block(64);
     if (out_f32)
         ln_kernel<NV, true><<<grid, block, 0, s>>>(x, g, b, y, rows, d, eps);
     else
