@@ -90,16 +90,29 @@ size_t wenc_weights_nbytes(const wenc_config *cfg);
 
 /* Copy a HOST blob (layout above) into the device arena, repacking it once
  * (conv taps to [out][k][in], q|k|v concatenated with a zero k bias, gains,
- * biases and positions widened exactly to fp32) in one upload.  nbytes must
- * equal wenc_weights_nbytes.  Synchronous; may be called again between
- * forwards to replace the weights.  The blob is not retained. */
+ * biases and positions widened exactly to fp32) in one upload.  The blob is
+ * read for the upload and not retained, and the matrix weights stay fp16 on
+ * the device (whisper README, "Performance and memory": the checkpoint is
+ * mapped for the upload and released, f16 weights stay f16; whisper 0.9.0
+ * API page, wh_open: one device arena per model, freed as a whole).
+ * nbytes must equal wenc_weights_nbytes, else WENC_EINVAL with nothing
+ * changed.  Synchronous.  May be called again to replace the weights: it
+ * first waits for all work already enqueued on the device (on any stream)
+ * to finish, so a forward still in flight reads the old weights to its
+ * end.  If the upload fails (WENC_EHIP) the handle counts as not loaded
+ * and wenc_forward returns WENC_ESTATE until a later wenc_load succeeds
+ * (whisper README, "Implementation notes": a failure is reported, never
+ * run past). */
 int wenc_load(wenc_t *h, const void *blob, size_t nbytes);
 
 /* out[b] = encoder(mel[b]) for b < batch.
  *   mel: device, fp32 [batch][n_frames][n_mels], a frame contiguous
- *        (whisper 0.9.0 API page, wh_encode).
- *   out: device, fp32 [batch][n_ctx][d_model] row-major (wh_enc_out).
+ *        (whisper 0.9.0 API page, wh_encode); 16-byte aligned.
+ *   out: device, fp32 [batch][n_ctx][d_model] row-major (wh_enc_out);
+ *        16-byte aligned.
  * batch == 0 is a no-op; batch > max_batch runs in chunks of max_batch.
+ * WENC_EINVAL (before any launch) for a NULL or misaligned pointer or
+ * batch < 0; WENC_ESTATE before a successful wenc_load.
  * Enqueued on `stream`; no host synchronisation. */
 int wenc_forward(wenc_t *h, const float *mel, int32_t batch, float *out, void *stream);
 
@@ -108,20 +121,28 @@ int wenc_forward(wenc_t *h, const float *mel, int32_t batch, float *out, void *s
  * 30 s window, as whisper.cpp's audio_ctx does).  The same encoder runs over
  * 2 * n_ctx frames and adds the FIRST n_ctx rows of the stored position
  * table; attention spans those n_ctx positions only.
- *   mel: device, fp32 [batch][2 * n_ctx][n_mels];
- *   out: device, fp32 [batch][n_ctx][d_model].
- * 1 <= n_ctx <= the configured n_ctx, else WENC_EINVAL before any launch;
+ *   mel: device, fp32 [batch][2 * n_ctx][n_mels], 16-byte aligned;
+ *   out: device, fp32 [batch][n_ctx][d_model], 16-byte aligned.
+ * 1 <= n_ctx <= the configured n_ctx, else WENC_EINVAL before any launch
+ * (as for a NULL or misaligned pointer);
  * n_ctx equal to the configured one is wenc_forward.  Windows are chunked by
  * what the scratch holds at this length (more than max_batch when n_ctx is
  * shorter).  Enqueued on `stream`; no host synchronisation. */
 int wenc_forward_ctx(wenc_t *h, const float *mel, int32_t batch, int32_t n_ctx, float *out, void *stream);
 
-/* Release the handle and its device memory.  NULL-safe.  Synchronises the
- * device first so no enqueued work still uses the memory. */
+/* Release the handle and every device allocation it owns (whisper 0.9.0
+ * API page, wh_close, and the Whisper struct's list of every device
+ * allocation kept for the free).  NULL-safe.  Synchronises the device first
+ * so no enqueued work still uses the memory.  The handle must not be used
+ * afterwards. */
 void wenc_destroy(wenc_t *h);
 
 /* Message for the last failure on `h` (or of wenc_create / handle-less calls
- * in this thread when h is NULL).  Never NULL; "" when there is none. */
+ * in this thread when h is NULL): the library's failures come back as a
+ * status code plus a message, as wh_open on the whisper 0.9.0 API page
+ * returns either the model or an error string.  Never NULL; "" when there
+ * is none.  The pointer stays valid until the next failing call on the
+ * same handle (or, for h == NULL, in the same thread). */
 const char *wenc_last_error(const wenc_t *h);
 
 /* Log-mel spectrogram of whole windows, the encoder's input (CKE page, "The
@@ -131,8 +152,10 @@ const char *wenc_last_error(const wenc_t *h);
  * over 0 .. 8 kHz; log10 of max(power, 1e-10); clamp at the window's maximum
  * minus 8 (-80 dB); (x + 4) / 4.  All in fp32.
  *   audio: device fp32 [batch][160 * n_frames], 16 kHz mono, already padded
- *          or cut to the window (480,000 samples for 3000 frames);
- *   mel:   device fp32 [batch][n_frames][n_mels], wenc_forward's input.
+ *          or cut to the window (480,000 samples for 3000 frames); 4-byte
+ *          aligned;
+ *   mel:   device fp32 [batch][n_frames][n_mels], wenc_forward's input;
+ *          16-byte aligned (else WENC_EINVAL before any launch).
  * Needs n_mels a multiple of 8, <= 128 (Whisper uses 80 and 128), else
  * WENC_EINVAL.  batch > max_batch runs in chunks.  Enqueued on `stream`. */
 int wenc_log_mel(wenc_t *h, const float *audio, int32_t batch, float *mel, void *stream);
@@ -159,7 +182,8 @@ int wenc_load_cross(wenc_t *h, int32_t n_dec_layer, const void *blob, size_t nby
  *   xk[l][b] = memory[b] . x_wk[l]^T,  xv[l][b] = memory[b] . x_wv[l]^T + x_bv[l].
  *   memory: device fp32 [batch][n_ctx][d_model] (wenc_forward's or
  *           wenc_forward_ctx's out), rounded to fp16 once before use;
- *   xk, xv: device fp16 [n_dec_layer][batch][n_ctx][d_model] each.
+ *   xk, xv: device fp16 [n_dec_layer][batch][n_ctx][d_model] each;
+ *   all three 16-byte aligned (else WENC_EINVAL before any launch).
  * 1 <= n_ctx <= the configured n_ctx.  WENC_ESTATE before wenc_load_cross.
  * Uses the handle's scratch (no forward may overlap it).  Enqueued on
  * `stream`; no host synchronisation. */
@@ -271,8 +295,9 @@ int wenc_argmax(wenc_t *h, const float *logits, int32_t rows, int32_t n_vocab, i
  * its last 256-row tile rows to 128 x 128 tiles when that evens out the last
  * round over the compute units, 0 keeps one tile size.  Every configuration
  * sums each output over k in the same order, so all give the same bits.
- * Not thread-safe against concurrent GEMM launches; returns WENC_EINVAL for
- * values out of range. */
+ * The two values are stored atomically: a launch on another thread sees
+ * each one either before or after the change (so it may pair a new tile
+ * with an old split).  Returns WENC_EINVAL for values out of range. */
 int wenc_k_gemm_mode(int32_t tile, int32_t split);
 
 /* Test-only, host logic (no device work): the tile plan wenc_k_gemm would use
@@ -309,7 +334,11 @@ enum {
     WENC_N_SITES = 16
 };
 int wenc_profile(wenc_t *h, uint32_t site_mask);
-/* ms_total[s] and launches[s] for s < WENC_N_SITES (arrays of that length). */
+/* ms_total[s] and launches[s] for s < WENC_N_SITES (arrays of that length):
+ * launches[s] counts the recorded launches of site s, and ms_total[s] is the
+ * time during which at least one of them was running (the length of the
+ * union of their intervals, so launches of one site that overlap on the
+ * streams of a split forward count once; on one stream it is the sum). */
 int wenc_profile_read(wenc_t *h, double *ms_total, int64_t *launches);
 
 #ifdef __cplusplus

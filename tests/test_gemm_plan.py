@@ -49,8 +49,8 @@ def test_plan_invariants(cus):
         for M in range(1, 70000, 997):
             kind, rows = wenc.wenc_k_gemm_plan(M, N, cus)
             tm, tn = math.ceil(M / 256), math.ceil(N / 256)
-            # big tiles only when they fill the CUs nearly twice over
-            assert (kind == SMALL) == (tm * tn < 448), (M, N, cus, kind)
+            # big tiles only when they fill the CUs at least 1.75 times over
+            assert (kind == SMALL) == (4 * tm * tn < 7 * cus), (M, N, cus, kind)
             if kind == BIG:
                 assert rows == M
             if kind == SPLIT:

@@ -183,3 +183,50 @@ def test_k_bias_is_unobservable(case, monkeypatch):
     cfg, mel, params, ref = case
     monkeypatch.setattr(enc, "mha", _mha_k_bias)
     assert np.abs(enc.encode(mel, params, cfg.n_layer, cfg.n_head) - ref).max() < 1e-9
+
+
+def _attn_mean_v(q, k, v):
+    # ignores the scores: every query gets the mean of the values
+    v = np.asarray(v, dtype=np.float64)
+    return np.repeat(v.mean(axis=0, keepdims=True), np.shape(q)[0], axis=0)
+
+
+def _bar_metrics(got, ref):
+    """The GPU tests' end-to-end statistics: min per-row cosine, max |err|
+    (the bar is cosine >= 0.9999 and max |err| <= 3e-2)."""
+    num = (got * ref).sum(1)
+    cos = (num / (np.linalg.norm(got, axis=1) * np.linalg.norm(ref, axis=1))).min()
+    return cos, np.abs(got - ref).max()
+
+
+def test_sharpened_workload_catches_mean_v_attention(monkeypatch):
+    """At the workloads' N(0, 0.02) weights an attention that returns mean(V)
+    comes close to the end-to-end bar (attention is nearly uniform there:
+    min row cosine still > 0.999 over the base-sized workload's six blocks,
+    and a one-block workload passes outright); on the same window with wq
+    and wk scaled x5 (the GPU test test_sharpened_attention_matches_oracle)
+    it misses the bar by orders of magnitude, so that GPU test pins
+    attention in place.  Base-sized workload, window 0."""
+    from whisper_audio_encoder_amd import synth
+    from whisper_audio_encoder_amd.configs import CONFIGS
+    cfg = CONFIGS["c2"]
+    mel, params = synth.make_inputs(cfg)
+    mel = mel[0]
+    sharp = synth.sharpen_attention(params, cfg.n_layer, 5.0)
+
+    def run(p):
+        return enc.encode(mel, p, cfg.n_layer, cfg.n_head, cfg.ln_eps)
+
+    plain_ref, sharp_ref = run(params), run(sharp)
+    # the scores of the sharpened first layer spread by a few units
+    lp = {f: np.asarray(sharp[f"l0.{f}"], dtype=np.float64) for f in ("wq", "bq", "wk")}
+    x0 = enc.gelu(enc.conv1d(enc.gelu(enc.conv1d(mel, params["conv1_w"], params["conv1_b"], 1)),
+                             params["conv2_w"], params["conv2_b"], 2)) + np.asarray(params["pos"], dtype=np.float64)
+    xn = enc.layer_norm(x0, params["l0.ln1_g"], params["l0.ln1_b"], cfg.ln_eps)
+    s = (xn @ lp["wq"].T + lp["bq"])[:, :64] @ (xn @ lp["wk"].T)[:, :64].T / 8.0
+    assert 2.0 < s.std() < 8.0, s.std()
+    monkeypatch.setattr(enc, "attention", _attn_mean_v)
+    cos, err = _bar_metrics(run(params), plain_ref)
+    assert cos > 0.999 and err < 0.2, (cos, err)
+    cos, err = _bar_metrics(run(sharp), sharp_ref)
+    assert cos < 0.95 and err > 0.5, (cos, err)

@@ -28,6 +28,8 @@
 // over the 8 XCDs) receives a contiguous run of tiles, ordered in groups of
 // a few tile rows (tile_coords), so tiles sharing A rows or W rows share
 // that XCD's L2.
+#include <algorithm>
+#include <atomic>
 #include <cstdlib>
 
 #include "common.h"
@@ -566,20 +568,40 @@ hipError_t launch_tagged(const GemmP &p, int epi, int tag, hipStream_t s) {
     return tag ? launch_cfg<BM, BN, WM, WN, NW, 1>(p, epi, s) : launch_cfg<BM, BN, WM, WN, NW, 0>(p, epi, s);
 }
 
-int g_tile_override = -1;  // WENC_GEMM_TILE: 0 = 128x128 x 4 waves, 1 = 256x256 x 8 waves
-int g_split = 1;            // WENC_GEMM_SPLIT=0 keeps a launch on one tile size
+// Tile configuration shared by every launch in the process (a test-only
+// override): tile 0 = 128x128 x 4 waves, 1 = 256x256 x 8 waves, anything
+// else = chosen per launch; split 0 keeps a launch on one tile size.  The
+// environment (WENC_GEMM_TILE, WENC_GEMM_SPLIT) is read once, under the
+// thread-safe initialisation of a function-local static; later changes go
+// through gemm_mode.  Atomics, so launches on other threads read a whole
+// value.
+struct TileMode {
+    std::atomic<int> tile, split;
+    TileMode() {
+        const char *e = std::getenv("WENC_GEMM_TILE");
+        const char *f = std::getenv("WENC_GEMM_SPLIT");
+        tile.store(e ? std::atoi(e) : 99);
+        split.store(f ? std::atoi(f) : 1);
+    }
+};
 
-// Compute units of the current device (cached per device).
+TileMode &tile_mode() {
+    static TileMode m;
+    return m;
+}
+
+// Compute units of the current device (cached per device; a race only
+// stores the same value twice).
 long cu_count() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 }  // namespace
@@ -590,8 +612,8 @@ int gemm_mode(int tile, int split) {
         const char *e = std::getenv("WENC_GEMM_TILE");
         tile = e ? std::atoi(e) : 99;
     }
-    g_tile_override = tile;
-    g_split = split;
+    tile_mode().tile.store(tile);
+    tile_mode().split.store(split);
     return 0;
 }
 
@@ -646,7 +668,7 @@ const char *gemm_check(const wenc_gemm_args &a) {
     return nullptr;
 }
 
-hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag) {
+hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag, int cu_div) {
     if (a.M == 0) return hipSuccess;
     GemmP p{};
     p.A = reinterpret_cast<const f16 *>(a.A);
@@ -689,14 +711,8 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag) {
         p.a_valid = a.T;
         p.t_div = make_divu(tp);
     }
-    if (g_tile_override < 0) {
-        const char *e = std::getenv("WENC_GEMM_TILE");
-        g_tile_override = e ? std::atoi(e) : 99;
-        const char *f = std::getenv("WENC_GEMM_SPLIT");
-        g_split = f ? std::atoi(f) : 1;
-    }
-    const GemmPlan plan = gemm_plan(p.M, p.N, cu_count(), g_tile_override == 0 || g_tile_override == 1 ? g_tile_override : -1,
-                                    g_split);
+    const int tile = tile_mode().tile.load(), split = tile_mode().split.load();
+    const GemmPlan plan = gemm_plan(p.M, p.N, std::max(1L, cu_count() / std::max(cu_div, 1)), tile == 0 || tile == 1 ? tile : -1, split);
     if (plan.kind == GEMM_PLAN_SMALL) return launch_tagged<128, 128, 64, 64, 4>(p, a.epilogue, tag, s);
     if (plan.kind == GEMM_PLAN_BIG) return launch_tagged<256, 256, 128, 64, 8>(p, a.epilogue, tag, s);
     GemmP big = p;
@@ -711,11 +727,11 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag) {
 GemmPlan gemm_plan(int M, int N, long cus, int tile, int split) {
     if (tile == 1) return {GEMM_PLAN_BIG, M};
     if (tile == 0) return {GEMM_PLAN_SMALL, 0};
-    // 256 x 256 tiles when they fill the CUs nearly twice over (measured: on
-    // 24000 x 768 x {768, 3072}, 282 such tiles, the 128 x 128 tiles at two
-    // workgroups per CU are 10-20% faster).
+    // 256 x 256 tiles when they fill the CUs at least 1.75 times over
+    // (measured on 256 CUs: on 24000 x 768 x {768, 3072}, 282 such tiles,
+    // the 128 x 128 tiles at two workgroups per CU are 10-20% faster).
     const long tn_big = (N + 255) / 256, tm_big = (long(M) + 255) / 256;
-    if (tm_big * tn_big < 448) return {GEMM_PLAN_SMALL, 0};
+    if (4 * tm_big * tn_big < 7 * cus) return {GEMM_PLAN_SMALL, 0};
     // The 256 x 256 kernel runs one tile per CU at a time, so a tile count
     // just past a multiple of the CU count leaves most CUs idle in the last
     // round.  Then the last tile rows go to the 128 x 128 kernel instead (two

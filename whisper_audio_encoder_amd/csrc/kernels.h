@@ -9,8 +9,10 @@ namespace wk {
 // Checks the shape/alignment contract of wenc_gemm_args; returns a message
 // or nullptr when the arguments are acceptable.
 const char *gemm_check(const wenc_gemm_args &a);
-// tag 1 selects a separately named copy of the kernel (fc1, fc2).
-hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag = 0);
+// tag 1 selects a separately named copy of the kernel (fc1, fc2); the tile
+// plan is made for the device's compute units divided by cu_div (the share
+// of one stream when two streams run GEMMs side by side).
+hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag = 0, int cu_div = 1);
 // Tile configuration of later launches (see wenc_k_gemm_mode); -1 if out of range.
 int gemm_mode(int tile, int split);
 // Tile plan of one GEMM launch over M rows (as the kernel sees them) and N

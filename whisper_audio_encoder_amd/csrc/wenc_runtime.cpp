@@ -202,6 +202,10 @@ FrontendTables frontend_tables(int n_mels) {
     return t;
 }
 
+// True when p is not a multiple of `align` bytes (the kernels' vector
+// loads and stores need 16-byte aligned fp32 rows).
+bool misaligned(const void *p, uintptr_t align) { return (reinterpret_cast<uintptr_t>(p) & (align - 1)) != 0; }
+
 struct ProfRec {
     int site;
     hipEvent_t e0, e1;
@@ -227,6 +231,13 @@ struct wenc {
     uint32_t prof_mask = 0;
     std::vector<ProfRec> prof_pending;
     std::vector<hipEvent_t> event_pool;
+    // Streams of a split forward beside the caller's, with the events that
+    // fork them from it and join them back (created with the handle, at the
+    // default priority).
+    static constexpr int MAX_PARTS = 4;
+    hipStream_t aux[MAX_PARTS - 1] = {};
+    hipEvent_t ev_fork = nullptr, ev_join[MAX_PARTS - 1] = {};
+    int n_parts = 2;  // a chunk's windows are split over this many streams
 
     template <class T>
     T *W(size_t off) const { return reinterpret_cast<T *>(warena + off); }
@@ -272,6 +283,8 @@ struct wenc {
     }
 
     int forward_chunk(const float *mel, int nb, int T, float *out, hipStream_t st, int tap, void *tap_dst);
+    int forward_part(const float *mel, int b0, int nb, int T, float *out, hipStream_t st, int cu_div, int tap,
+                     void *tap_dst);
     int chunk_cap(int T) const;
 };
 
@@ -292,15 +305,60 @@ int wenc::chunk_cap(int T) const {
     return int(std::max<int64_t>(cap, 1));
 }
 
+// One chunk of nb windows (mel [nb][2T][n_mels] -> out [nb][T][d]).  Unless
+// a tap is asked for, the windows are split into n_parts groups that each
+// run the whole path on a stream of their own: the first group on the
+// caller's stream, the others on the handle's streams, forked from the
+// caller's stream with an event and joined back before the call returns.
+// The groups use disjoint window slices of the scratch.  Their kernels
+// share the device, so one group's LayerNorms, residual epilogues and last
+// partial round of tiles overlap another group's work, and every output is
+// computed exactly as in one launch over all windows: windows are
+// independent, and no kernel's per-element arithmetic depends on the batch.
 int wenc::forward_chunk(const float *mel, int nb, int T, float *out, hipStream_t st, int tap, void *tap_dst) {
+    const int parts = tap >= 0 ? 1 : std::max(1, std::min(n_parts, nb));
+    if (parts == 1) return forward_part(mel, 0, nb, T, out, st, 1, tap, tap_dst);
+    const size_t F = 2 * size_t(T);
+    hipError_t e = hipEventRecord(ev_fork, st);
+    for (int i = 0; i + 1 < parts && e == hipSuccess; ++i) e = hipStreamWaitEvent(aux[i], ev_fork, 0);
+    if (e != hipSuccess) return fail(&err, WENC_EHIP, "forward: stream fork: %s", hipGetErrorString(e));
+    int rc = WENC_OK, joined = 0;
+    for (int i = 0; i < parts; ++i) {
+        const int b0 = int(int64_t(nb) * i / parts), b1 = int(int64_t(nb) * (i + 1) / parts);
+        hipStream_t si = i == 0 ? st : aux[i - 1];
+        rc = forward_part(mel + size_t(b0) * F * cfg.n_mels, b0, b1 - b0, T, out + size_t(b0) * T * cfg.d_model, si,
+                          parts, -1, nullptr);
+        if (i > 0) ++joined;
+        if (rc != WENC_OK) break;
+    }
+    // join every stream that received work, also after a failure, so the
+    // caller's stream never runs ahead of work enqueued on the others
+    for (int i = 0; i < joined; ++i) {
+        hipError_t ej = hipEventRecord(ev_join[i], aux[i]);
+        if (ej == hipSuccess) ej = hipStreamWaitEvent(st, ev_join[i], 0);
+        if (ej != hipSuccess && e == hipSuccess) e = ej;
+    }
+    if (rc != WENC_OK) return rc;
+    if (e != hipSuccess) return fail(&err, WENC_EHIP, "forward: stream join: %s", hipGetErrorString(e));
+    return WENC_OK;
+}
+
+// Windows [b0, b0 + nb) of the chunk, on stream st, with the GEMM tile plan
+// made for cus / cu_div compute units (the share one stream of a pipelined
+// chunk can expect).
+int wenc::forward_part(const float *mel, int b0, int nb, int T, float *out, hipStream_t st, int cu_div, int tap,
+                       void *tap_dst) {
     const wenc_config &c = cfg;
     const int F = 2 * T, nm = c.n_mels, d = c.d_model, H = c.n_head, Fd = c.d_ff;
     const int M = nb * T;
     const int ldvt = (T + 63) / 64 * 64;
-    uint16_t *melp = S<uint16_t>(sl.melp), *c1 = S<uint16_t>(sl.c1), *xn = S<uint16_t>(sl.xn);
-    uint16_t *q = S<uint16_t>(sl.q), *k = S<uint16_t>(sl.k), *vt = S<uint16_t>(sl.vt);
-    uint16_t *ao = S<uint16_t>(sl.ao), *hb = S<uint16_t>(sl.hbuf);
-    float *x = S<float>(sl.x);
+    const size_t wb = size_t(b0);  // window offset into the densely packed scratch
+    uint16_t *melp = S<uint16_t>(sl.melp) + wb * (F + 2) * nm, *c1 = S<uint16_t>(sl.c1) + wb * (F + 2) * d;
+    uint16_t *xn = S<uint16_t>(sl.xn) + wb * T * d;
+    uint16_t *q = S<uint16_t>(sl.q) + wb * H * T * 64, *k = S<uint16_t>(sl.k) + wb * H * T * 64;
+    uint16_t *vt = S<uint16_t>(sl.vt) + wb * H * 64 * ldvt;
+    uint16_t *ao = S<uint16_t>(sl.ao) + wb * T * d, *hb = S<uint16_t>(sl.hbuf) + wb * T * Fd;
+    float *x = S<float>(sl.x) + wb * T * d;
 
     WENC_TRY(site(WENC_SITE_INGEST, st, [&] { return wk::launch_ingest(mel, melp, c1, nb, F, nm, d, st); }));
 
@@ -322,7 +380,7 @@ int wenc::forward_chunk(const float *mel, int nb, int T, float *out, hipStream_t
     g.N = d;
     g.K = 3 * nm;
     g.epilogue = WENC_EPI_GELU_F16;
-    WENC_TRY(site(WENC_SITE_CONV1, st, [&] { return wk::launch_gemm(g, st); }));
+    WENC_TRY(site(WENC_SITE_CONV1, st, [&] { return wk::launch_gemm(g, st, 0, cu_div); }));
     if (tap == WENC_TAP_C1) {
         const hipError_t e = hipMemcpy2DAsync(tap_dst, size_t(F) * d * 2, c1 + d, size_t(F + 2) * d * 2,
                                               size_t(F) * d * 2, nb, hipMemcpyDeviceToDevice, st);
@@ -346,7 +404,7 @@ int wenc::forward_chunk(const float *mel, int nb, int T, float *out, hipStream_t
     g.N = d;
     g.K = 3 * d;
     g.epilogue = WENC_EPI_CONV2;
-    WENC_TRY(site(WENC_SITE_CONV2, st, [&] { return wk::launch_gemm(g, st); }));
+    WENC_TRY(site(WENC_SITE_CONV2, st, [&] { return wk::launch_gemm(g, st, 0, cu_div); }));
     auto copy_x = [&](void *dst) {
         const hipError_t e = hipMemcpyAsync(dst, x, size_t(M) * d * 4, hipMemcpyDeviceToDevice, st);
         return e == hipSuccess ? WENC_OK : fail(&err, WENC_EHIP, "tap copy: %s", hipGetErrorString(e));
@@ -378,7 +436,7 @@ int wenc::forward_chunk(const float *mel, int nb, int T, float *out, hipStream_t
         g.N = 3 * d;
         g.K = d;
         g.epilogue = WENC_EPI_QKV;
-        WENC_TRY(site(WENC_SITE_QKV, st, [&] { return wk::launch_gemm(g, st); }));
+        WENC_TRY(site(WENC_SITE_QKV, st, [&] { return wk::launch_gemm(g, st, 0, cu_div); }));
         WENC_TRY(site(WENC_SITE_ATTN, st, [&] { return wk::launch_attention(q, k, vt, ao, nb, H, T, ldvt, st); }));
         g = wenc_gemm_args{};
         g.A = ao;
@@ -394,7 +452,7 @@ int wenc::forward_chunk(const float *mel, int nb, int T, float *out, hipStream_t
         g.N = d;
         g.K = d;
         g.epilogue = WENC_EPI_RESID;
-        WENC_TRY(site(WENC_SITE_OPROJ, st, [&] { return wk::launch_gemm(g, st); }));
+        WENC_TRY(site(WENC_SITE_OPROJ, st, [&] { return wk::launch_gemm(g, st, 0, cu_div); }));
         WENC_TRY(site(WENC_SITE_LN2, st, [&] {
             return wk::launch_layernorm(x, W<float>(lo.ln2_g), W<float>(lo.ln2_b), xn, M, d, c.ln_eps, false, st);
         }));
@@ -414,7 +472,7 @@ int wenc::forward_chunk(const float *mel, int nb, int T, float *out, hipStream_t
         g.N = Fd;
         g.K = d;
         g.epilogue = WENC_EPI_GELU_F16;
-        WENC_TRY(site(WENC_SITE_FC1, st, [&] { return wk::launch_gemm(g, st, 1); }));
+        WENC_TRY(site(WENC_SITE_FC1, st, [&] { return wk::launch_gemm(g, st, 1, cu_div); }));
         g = wenc_gemm_args{};
         g.A = hb;
         g.a_batch_stride = int64_t(T) * Fd;
@@ -429,7 +487,7 @@ int wenc::forward_chunk(const float *mel, int nb, int T, float *out, hipStream_t
         g.N = d;
         g.K = Fd;
         g.epilogue = WENC_EPI_RESID;
-        WENC_TRY(site(WENC_SITE_FC2, st, [&] { return wk::launch_gemm(g, st, 1); }));
+        WENC_TRY(site(WENC_SITE_FC2, st, [&] { return wk::launch_gemm(g, st, 1, cu_div); }));
         if (tap == WENC_TAP_BLOCK + l) return copy_x(tap_dst);
     }
 
@@ -440,6 +498,26 @@ int wenc::forward_chunk(const float *mel, int nb, int T, float *out, hipStream_t
         return WENC_OK;
     }
     return copy_x(out);
+}
+
+// Frees everything a handle owns (device memory, events, the stream) and
+// the handle; the device must be idle for it.
+static void release(wenc *h) {
+    for (auto &r : h->prof_pending) {
+        (void)hipEventDestroy(r.e0);
+        (void)hipEventDestroy(r.e1);
+    }
+    for (auto e : h->event_pool) (void)hipEventDestroy(e);
+    if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+    for (int i = 0; i + 1 < wenc::MAX_PARTS; ++i) {
+        if (h->ev_join[i]) (void)hipEventDestroy(h->ev_join[i]);
+        if (h->aux[i]) (void)hipStreamDestroy(h->aux[i]);
+    }
+    if (h->warena) (void)hipFree(h->warena);
+    if (h->sarena) (void)hipFree(h->sarena);
+    if (h->xarena) (void)hipFree(h->xarena);
+    if (h->farena) (void)hipFree(h->farena);
+    delete h;
 }
 
 extern "C" {
@@ -474,6 +552,10 @@ int wenc_create(const wenc_config *cfg, wenc_t **out) {
     h->sl = scratch_layout(*cfg);
     const char *dbg = std::getenv("WENC_DEBUG_SYNC");
     h->debug_sync = dbg && dbg[0] == '1';
+    // WENC_SPLIT_STREAMS=n splits a chunk's windows over n streams (1 keeps
+    // every launch on the caller's stream; at most MAX_PARTS).
+    if (const char *pp = std::getenv("WENC_SPLIT_STREAMS"))
+        h->n_parts = std::max(1, std::min(std::atoi(pp), int(wenc::MAX_PARTS)));
     auto alloc = [&](char **p, size_t bytes, const char *what) -> int {
         const hipError_t ea = hipMalloc(reinterpret_cast<void **>(p), bytes);
         if (ea != hipSuccess) {
@@ -486,7 +568,14 @@ int wenc_create(const wenc_config *cfg, wenc_t **out) {
         }
         return WENC_OK;
     };
-    int rc = alloc(&h->warena, h->wl.total, "weights");
+    int rc = WENC_OK;
+    e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
+    for (int i = 0; i + 1 < h->n_parts && e == hipSuccess; ++i) {
+        e = hipStreamCreateWithFlags(&h->aux[i], hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_join[i], hipEventDisableTiming);
+    }
+    if (e != hipSuccess) rc = fail(nullptr, WENC_EHIP, "wenc_create: stream or event: %s", hipGetErrorString(e));
+    if (rc == WENC_OK) rc = alloc(&h->warena, h->wl.total, "weights");
     if (rc == WENC_OK) rc = alloc(&h->sarena, h->sl.total, "activation scratch");
     if (rc == WENC_OK) {
         // WENC_POISON_SCRATCH=1 fills the activations with all-ones bytes (NaN
@@ -512,10 +601,7 @@ int wenc_create(const wenc_config *cfg, wenc_t **out) {
         }
     }
     if (rc != WENC_OK) {
-        if (h->warena) (void)hipFree(h->warena);
-        if (h->sarena) (void)hipFree(h->sarena);
-        if (h->farena) (void)hipFree(h->farena);
-        delete h;
+        release(h);
         return rc;
     }
     *out = h;
@@ -575,7 +661,18 @@ int wenc_load(wenc_t *h, const void *blob, size_t nbytes) {
     f32(h->wl.lnf_g, d);
     f32(h->wl.lnf_b, d);
     hipError_t e = hipSetDevice(h->device);
-    if (e == hipSuccess) e = hipMemcpy(h->warena, host.data(), host.size(), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(&h->err, WENC_EHIP, "wenc_load: hipSetDevice: %s", hipGetErrorString(e));
+    if (h->loaded) {
+        // A forward may still be queued on any stream (torch's side streams do
+        // not wait for the null stream's copy): let it finish on the old weights.
+        e = hipDeviceSynchronize();
+        if (e != hipSuccess)
+            return fail(&h->err, WENC_EHIP, "wenc_load: waiting for enqueued work: %s", hipGetErrorString(e));
+    }
+    // From here the arena holds neither the old nor (until the copy ends) the
+    // new weights: a failed upload leaves the handle unloaded.
+    h->loaded = false;
+    e = hipMemcpy(h->warena, host.data(), host.size(), hipMemcpyHostToDevice);
     if (e != hipSuccess) return fail(&h->err, WENC_EHIP, "wenc_load: upload failed: %s", hipGetErrorString(e));
     h->loaded = true;
     return WENC_OK;
@@ -591,6 +688,7 @@ static int forward_impl(wenc_t *h, const float *mel, int32_t batch, int32_t n_ct
         return fail(&h->err, WENC_EINVAL, "wenc_forward_ctx: n_ctx %d outside [1, %d]", n_ctx, c.n_ctx);
     if (batch == 0) return WENC_OK;
     if (!mel) return fail(&h->err, WENC_EINVAL, "wenc_forward: mel is NULL");
+    if (misaligned(mel, 16)) return fail(&h->err, WENC_EINVAL, "wenc_forward: mel must be 16-byte aligned");
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (tap >= 0) {
         if (!tap_dst) return fail(&h->err, WENC_EINVAL, "wenc_forward_tap: dst is NULL");
@@ -601,6 +699,7 @@ static int forward_impl(wenc_t *h, const float *mel, int32_t batch, int32_t n_ct
         return h->forward_chunk(mel, batch, n_ctx, nullptr, st, tap, tap_dst);
     }
     if (!out) return fail(&h->err, WENC_EINVAL, "wenc_forward: out is NULL");
+    if (misaligned(out, 16)) return fail(&h->err, WENC_EINVAL, "wenc_forward: out must be 16-byte aligned");
     const int cap = h->chunk_cap(n_ctx);
     for (int b0 = 0; b0 < batch; b0 += cap) {
         const int nb = batch - b0 < cap ? batch - b0 : cap;
@@ -684,6 +783,8 @@ int wenc_prepare_cross(wenc_t *h, const float *memory, int32_t batch, int32_t n_
         return fail(&h->err, WENC_EINVAL, "wenc_prepare_cross: n_ctx %d outside [1, %d]", n_ctx, c.n_ctx);
     if (batch == 0) return WENC_OK;
     if (!memory || !xk || !xv) return fail(&h->err, WENC_EINVAL, "wenc_prepare_cross: memory, xk and xv must be non-null");
+    if (misaligned(memory, 16) || misaligned(xk, 16) || misaligned(xv, 16))
+        return fail(&h->err, WENC_EINVAL, "wenc_prepare_cross: memory, xk and xv must be 16-byte aligned");
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int d = c.d_model, T = n_ctx;
     const int cap = h->chunk_cap(T);
@@ -784,6 +885,8 @@ int wenc_log_mel(wenc_t *h, const float *audio, int32_t batch, float *mel, void 
     if (!h->farena) return fail(&h->err, WENC_ESTATE, "wenc_log_mel: frontend tables missing");
     if (batch == 0) return WENC_OK;
     if (!audio || !mel) return fail(&h->err, WENC_EINVAL, "wenc_log_mel: audio and mel must be non-null");
+    if (misaligned(audio, 4) || misaligned(mel, 16))
+        return fail(&h->err, WENC_EINVAL, "wenc_log_mel: audio must be 4-byte and mel 16-byte aligned");
     hipStream_t st = static_cast<hipStream_t>(stream);
     const float *tab = reinterpret_cast<const float *>(h->farena);
     const float *win = reinterpret_cast<const float *>(h->farena + h->f_win);
@@ -802,17 +905,9 @@ int wenc_log_mel(wenc_t *h, const float *audio, int32_t batch, float *mel, void 
 void wenc_destroy(wenc_t *h) {
     if (!h) return;
     // teardown: errors cannot be acted on here, every release is attempted
+    (void)hipSetDevice(h->device);
     (void)hipDeviceSynchronize();
-    for (auto &r : h->prof_pending) {
-        (void)hipEventDestroy(r.e0);
-        (void)hipEventDestroy(r.e1);
-    }
-    for (auto e : h->event_pool) (void)hipEventDestroy(e);
-    if (h->warena) (void)hipFree(h->warena);
-    if (h->sarena) (void)hipFree(h->sarena);
-    if (h->xarena) (void)hipFree(h->xarena);
-    if (h->farena) (void)hipFree(h->farena);
-    delete h;
+    release(h);
 }
 
 const char *wenc_last_error(const wenc_t *h) {
@@ -870,17 +965,38 @@ int wenc_profile_read(wenc_t *h, double *ms_total, int64_t *launches) {
         launches[s] = 0;
     }
     int rc = WENC_OK;
+    // Each launch as an interval [start, end] in ms after the first recorded
+    // event; a site's time is the length of the union of its intervals, so
+    // launches of one site that overlap on different streams count once.
+    std::vector<std::vector<std::pair<float, float>>> iv(WENC_N_SITES);
+    const hipEvent_t ref = h->prof_pending.empty() ? nullptr : h->prof_pending.front().e0;
     for (auto &r : h->prof_pending) {
-        float ms = 0.f;
+        float t0 = 0.f, t1 = 0.f;
         hipError_t e = hipEventSynchronize(r.e1);
-        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.e0, r.e1);
+        if (e == hipSuccess) e = hipEventElapsedTime(&t0, ref, r.e0);
+        if (e == hipSuccess) e = hipEventElapsedTime(&t1, ref, r.e1);
         if (e != hipSuccess && rc == WENC_OK) rc = fail(&h->err, WENC_EHIP, "wenc_profile_read: %s", hipGetErrorString(e));
-        ms_total[r.site] += ms;
+        if (e == hipSuccess) iv[r.site].push_back({t0, std::max(t0, t1)});
         launches[r.site] += 1;
         h->event_pool.push_back(r.e0);
         h->event_pool.push_back(r.e1);
     }
     h->prof_pending.clear();
+    for (int s = 0; s < WENC_N_SITES; ++s) {
+        std::sort(iv[s].begin(), iv[s].end());
+        double total = 0.0, lo = 0.0, hi = -1.0;
+        for (const auto &x : iv[s]) {
+            if (x.first > hi) {
+                if (hi >= lo) total += hi - lo;
+                lo = x.first;
+                hi = x.second;
+            } else {
+                hi = std::max<double>(hi, x.second);
+            }
+        }
+        if (hi >= lo) total += hi - lo;
+        ms_total[s] = total;
+    }
     return rc;
 }
 

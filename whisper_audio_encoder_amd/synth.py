@@ -94,6 +94,20 @@ def make_inputs(cfg: EncoderConfig, batch: int | None = None, seed: int | None =
     return mel, params
 
 
+def sharpen_attention(params: dict, n_layer: int, factor: float) -> dict:
+    """A copy of params with every layer's wq and wk multiplied by `factor`
+    and rounded back to fp16 (the same bytes then feed both sides).  At the
+    workloads' N(0, 0.02) weights the scores spread by only ~0.15, so the
+    softmax is nearly uniform; x5 on both (x25 on the scores) gives a score
+    spread of a few units, where attention picks out keys."""
+    out = dict(params)
+    for li in range(n_layer):
+        for f in ("wq", "wk"):
+            w = np.asarray(params[f"l{li}.{f}"], dtype=np.float32) * np.float32(factor)
+            out[f"l{li}.{f}"] = w.astype(np.float16)
+    return out
+
+
 def pack_blob(cfg: EncoderConfig, params: dict) -> np.ndarray:
     """Concatenate parameters in canonical order into one uint8 blob."""
     parts = []
