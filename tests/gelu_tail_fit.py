@@ -1,13 +1,15 @@
-"""Coefficients of the GELU in common.h (gelu_erf), and their error check.
+"""How the coefficients of the kernels' GELU (gelu_erf in
+whisper_audio_encoder_amd/csrc/common.h) were derived.
 
 gelu(z) = z Phi(z) = max(z, 0) - |z| Q(|z|), where Q(u) = Phi(-u) is the
 upper tail of the standard normal distribution.  The kernel evaluates
-Q(u) = 2^p(u) with p a degree-5 polynomial in u; this script fits p to
-log2 Q on [0, 6] by iteratively reweighted least squares that drives down
-the largest absolute error of u Q(u) (the error the GELU inherits), rounds
-the coefficients to fp32, and checks in fp32 arithmetic that the GELU error
-stays small for every z and that p decreases (so the tail term keeps
-shrinking past the fitted range).  Run: python gelu_tail_fit.py
+Q(u) = 2^p(u) with p a degree-5 polynomial in u; fit() fits p to log2 Q on
+[0, 6] by iteratively reweighted least squares that drives down the largest
+absolute error of u Q(u) (the error the GELU inherits) and rounds the
+coefficients to fp32.  tests/test_gelu_constants.py checks the committed
+coefficients (parsed from common.h) against the exact GELU and for
+monotonicity; this script reproduces them:
+    python tests/gelu_tail_fit.py
 """
 import numpy as np
 from numpy.polynomial import polynomial as P

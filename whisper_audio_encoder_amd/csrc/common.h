@@ -37,8 +37,10 @@ __device__ __forceinline__ uint32_t divu(uint32_t n, const DivU &v) {
 // Phi(z) = 1 - Q(|z|) for z >= 0 and Q(|z|) for z < 0, so in both cases
 // gelu(z) = max(z, 0) - |z| Q(|z|).  Q is evaluated as 2^p(u), p a degree-5
 // polynomial fitted to log2 Q on [0, 6] so as to minimise the largest error
-// of u Q(u) (gelu_tail_fit.py beside this file derives the coefficients and
-// checks them): five FMAs, one exp2, one max and one FMA.  In fp32 the result
+// of u Q(u) (tests/gelu_tail_fit.py derives the coefficients, and
+// tests/test_gelu_constants.py checks the ones below against the exact GELU
+// in the same fp32 arithmetic): five FMAs, one exp2, one max and one FMA.
+// In fp32 the result
 // is within 4.7e-7 of the exact GELU everywhere (dense grid over [-12, 12]);
 // p decreases for all u >= 0, so past the fitted range the tail term keeps
 // shrinking (< 5e-9 beyond u = 6) and exp2 underflows to 0 for large |z|,
