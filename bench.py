@@ -289,40 +289,25 @@ def time_cross(enc, model, memory, n_dec, steps):
                                    "gb_per_s": am_bytes / (am_launch * 1e-3) / 1e9}}
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c4", choices=["c0", "c1", "c2", "c3", "c4"])
-    ap.add_argument("--batch", type=int, default=None, help="override the workload's batch")
-    ap.add_argument("--n-ctx", type=int, default=None,
-                    help="shortened context (drafts): encode 2*N_CTX frames per window with the full model")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--frontend", action="store_true",
-                    help="also time the log-mel frontend on the same number of synthetic 30-s windows")
-    ap.add_argument("--cross", type=int, default=None, metavar="N_DEC",
-                    help="also time the cross-attention K/V projection of N_DEC decoder layers from the output")
-    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
-                    help="only run a plain copy of BYTES (counter calibration) and exit")
-    a = ap.parse_args(argv)
-    if a.copy_probe:
-        copy_probe(a.copy_probe)
-        return
-    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the encoder shards by window (pure data parallelism, no "
-              "collective), and this build runs and reports a single MI355X only", file=sys.stderr)
-        sys.exit(2)
+def site_launches_per_step(cfg, site):
+    """How many times a site runs over the whole batch in one step."""
+    return cfg.n_layer if site in ("ln1", "qkv", "attn", "oproj", "ln2", "fc1", "fc2") else 1
 
+
+def run_workload(name, a, with_cpu):
+    """Time `steps` forwards of one workload's batch (after `warmup`) and
+    return its measurements: throughput, the dominant kernel's roofline
+    from events over the timed region, per-call and hipGraph figures, and
+    the oracle's CPU baseline."""
     import torch
     from whisper_audio_encoder_amd import synth, wenc
     from whisper_audio_encoder_amd.configs import CONFIGS, WORKLOAD_NAMES
 
-    model = CONFIGS[a.workload]
+    model = CONFIGS[name]
     B = a.batch or model.batch
     # cfg: the shape each window is encoded at (a draft runs the same model over fewer positions)
     cfg = model if a.n_ctx is None else model.with_(n_ctx=a.n_ctx, n_frames=2 * a.n_ctx)
-    log(f"[bench] workload {a.workload}: {WORKLOAD_NAMES[a.workload]}; running batch {B}"
+    log(f"[bench] workload {name}: {WORKLOAD_NAMES[name]}; running batch {B}"
         + ("" if a.n_ctx is None else f", drafts of {a.n_ctx} positions"))
     mel, params = synth.make_inputs(model, batch=B)
     mel = np.ascontiguousarray(mel[:, :cfg.n_frames])
@@ -343,7 +328,6 @@ def main(argv=None):
         enc.forward(mel_d, out, n_ctx=n_ctx)
     torch.cuda.synchronize()
     warm = wenc.wenc_profile_read(enc.h)
-    mfma_sites = [s for s in wenc.SITES if site_work(cfg, B)[s][0] == "mfma"]
     dominant = max(wenc.SITES, key=lambda s: warm[s][0])
     total_warm = sum(v[0] for v in warm.values()) or 1.0
     log("[bench] per-site share of kernel time (warm-up): " +
@@ -363,7 +347,7 @@ def main(argv=None):
     ms = e0.elapsed_time(e1) / a.steps
     prof = wenc.wenc_profile_read(enc.h)
     wenc.wenc_profile(enc.h, 0)
-    log(f"[bench] {a.steps} steps: {ms:.3f} ms/step (wall {1e3 * wall / a.steps:.3f} ms/step)")
+    log(f"[bench] {name}: {a.steps} steps: {ms:.3f} ms/step (wall {1e3 * wall / a.steps:.3f} ms/step)")
     # per-call times (median, minimum) from events around each forward
     per_call = []
     for _ in range(max(a.steps // 2, 3)):
@@ -375,48 +359,43 @@ def main(argv=None):
     torch.cuda.synchronize()
     call_ms = sorted(c0.elapsed_time(c1) for c0, c1 in per_call)
     graph = time_graph(enc, mel_d, out, n_ctx, a.steps)
-    log(f"[bench] hipGraph replay: {graph['ms_per_step']:.3f} ms/step")
+    log(f"[bench] {name}: hipGraph replay: {graph['ms_per_step']:.3f} ms/step")
 
     flops = cfg.flops_per_window() * B
     tflops = flops / (ms * 1e-3) / 1e12
+    # The dominant site over the whole batch: its algorithmic work per
+    # application (all windows) over the wall time it ran per application
+    # (the library's events give the union of its launches' intervals, so
+    # the launches of the split forward's streams, which overlap, count once).
     kind, work = site_work(cfg, B)[dominant]
     d_ms, d_n = prof[dominant]
-    avg_s = d_ms / max(d_n, 1) * 1e-3
+    per_step = site_launches_per_step(cfg, dominant)
+    avg_s = d_ms / (a.steps * per_step) * 1e-3
     if kind == "mfma":
         roof = {"bound": "mfma", "achieved": work / avg_s / 1e12, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": work / avg_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(a.workload, dominant)
+    roof["traffic"] = measured_traffic(name, dominant)
     roof["kernel"] = dominant
     roof["avg_launch_ms"] = avg_s * 1e3
     roof["launches"] = d_n
+    roof["applications"] = a.steps * per_step
 
     frontend = time_frontend(enc, model, B, a.steps) if a.frontend else None
-    cross = None
-    if a.cross:
-        cross = time_cross(enc, model, out, a.cross, a.steps)
+    cross = time_cross(enc, model, out, a.cross, a.steps) if a.cross else None
 
     cpu = None
-    if not a.no_cpu_baseline:
-        log("[bench] timing the fp64 oracle on one window ...")
+    if with_cpu:
+        log(f"[bench] {name}: timing the fp64 oracle on one window ...")
         cpu = cpu_baseline(cfg, mel, params)
         log(f"[bench] oracle: {cpu['value']:.4f} windows/s on {cpu['cores']} threads")
 
-    line = {
-        "metric": METRIC,
+    rec = {
         "value": B / (ms * 1e-3),
         "unit": "windows/s",
-        "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
         "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic (seeded mel N(-0.2,0.4) clamped, random-init fp16 weights)",
-        "config": {"workload": f"{WORKLOAD_NAMES[a.workload]} ({a.workload})"
+        "config": {"workload": f"{WORKLOAD_NAMES[name]} ({name})"
                    + ("" if n_ctx is None else f", drafts: {cfg.n_frames} frames per window"), "batch": B,
                    "n_frames": cfg.n_frames, "n_ctx": cfg.n_ctx, "d_model": cfg.d_model, "n_head": cfg.n_head,
                    "d_ff": cfg.d_ff, "n_layer": cfg.n_layer, "n_mels": cfg.n_mels, "parallelism": "single GPU"},
@@ -424,15 +403,74 @@ def main(argv=None):
         "pct_fp16_peak": 100.0 * tflops / PEAK_F16_TFLOPS,
         "per_call_ms": {"median": call_ms[len(call_ms) // 2], "min": call_ms[0], "calls": len(call_ms)},
         "graph_replay": graph,
-        "device_peak": device_peak(),
         "site_ms_per_step": {s: warm[s][0] / n_warm for s in wenc.SITES if warm[s][1]},
         "roofline": roof,
         "cpu_baseline": cpu,
         **({"cross_kv": cross} if cross else {}),
         **({"log_mel": frontend} if frontend else {}),
-        "host": platform.node(),
     }
     enc.close()
+    return rec
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4", choices=["c0", "c1", "c2", "c3", "c4"])
+    ap.add_argument("--also", default=None,
+                    help="comma-separated workloads measured after the headline one, each reported as a nested "
+                         "record under its name (default: c3 when the headline is c4, the other config the "
+                         "50%%-of-peak target names; '' for none)")
+    ap.add_argument("--batch", type=int, default=None, help="override the workload's batch")
+    ap.add_argument("--n-ctx", type=int, default=None,
+                    help="shortened context (drafts): encode 2*N_CTX frames per window with the full model")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--frontend", action="store_true",
+                    help="also time the log-mel frontend on the same number of synthetic 30-s windows")
+    ap.add_argument("--cross", type=int, default=None, metavar="N_DEC",
+                    help="also time the cross-attention K/V projection of N_DEC decoder layers from the output")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration) and exit")
+    a = ap.parse_args(argv)
+    if a.copy_probe:
+        copy_probe(a.copy_probe)
+        return
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the encoder shards by window (pure data parallelism, no "
+              "collective), and this build runs and reports a single MI355X only", file=sys.stderr)
+        sys.exit(2)
+    also = a.also
+    if also is None:
+        also = "c3" if a.workload == "c4" and a.batch is None and a.n_ctx is None else ""
+    also = [w for w in also.split(",") if w and w != a.workload]
+
+    head = run_workload(a.workload, a, not a.no_cpu_baseline)
+    nested = {}
+    for w in also:
+        sub = argparse.Namespace(**{**vars(a), "frontend": False, "cross": None})
+        rec = run_workload(w, sub, not a.no_cpu_baseline)
+        nested[w] = {"metric": METRIC, "steps": a.steps, "warmup": a.warmup, **rec}
+
+    line = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "windows/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded mel N(-0.2,0.4) clamped, random-init fp16 weights)",
+        **{k: v for k, v in head.items() if k not in ("value", "unit", "ms_per_step")},
+        "device_peak": device_peak(),
+        **nested,
+        "host": platform.node(),
+    }
     print(json.dumps(line), flush=True)
 
 

@@ -80,3 +80,21 @@ def test_bench_json_line():
     for part in (d, d["graph_replay"]):
         pc = part["per_call_ms"]
         assert 0 < pc["min"] <= pc["median"] and pc["calls"] >= 3
+
+
+@pytest.mark.gpu
+@pytest.mark.timeout(300)
+def test_bench_nested_workload_record():
+    """--also adds a nested record per extra workload on the same line, with
+    its own throughput, roofline and CPU baseline."""
+    r = _run_bench(["--workload", "c1", "--also", "c0", "--steps", "3", "--warmup", "2"])
+    assert r.returncode == 0, r.stderr[-3000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1, r.stdout
+    d = json.loads(lines[0])
+    assert "c1" in d["config"]["workload"]
+    sub = d["c0"]
+    assert "c0" in sub["config"]["workload"] and sub["steps"] == 3 and sub["warmup"] == 2
+    assert sub["value"] == pytest.approx(CONFIGS["c0"].batch / (sub["ms_per_step"] * 1e-3), rel=1e-9)
+    assert sub["roofline"]["achieved"] > 0 and sub["roofline"]["kernel"] in wenc.SITES
+    assert sub["cpu_baseline"]["kind"] == "oracle" and sub["cpu_baseline"]["value"] > 0
