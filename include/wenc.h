@@ -288,6 +288,22 @@ int wenc_cross_attend(wenc_t *h, const void *q, const void *xk, const void *xv, 
 int wenc_argmax(wenc_t *h, const float *logits, int32_t rows, int32_t n_vocab, int64_t ld, int32_t *out,
                 void *stream);
 
+/* wenc_argmax without a handle and without allocating: for callers that
+ * cannot allocate device memory (code being recorded into a HIP graph, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same result, arguments
+ * and error behaviour as wenc_argmax, whose kernels it runs; the per-chunk
+ * keys go to a 1 MiB array of 131072 keys that the library's code object
+ * holds on each device (kept until the process ends) instead of a handle's
+ * scratch, in passes of 131072 / ceil(n_vocab / 2048) rows.  No hipMalloc,
+ * hipFree or other allocating call is made.  Limit: ceil(n_vocab / 2048) <=
+ * 131072 (n_vocab <= 268435456), else WENC_EINVAL before any launch.  Every
+ * call on one device shares that device's array: calls that overlap on one
+ * device (on different streams or threads) race and may return wrong
+ * indices; calls in one stream's order are safe.  Errors are reported
+ * through wenc_last_error(NULL). */
+int wenc_argmax_noalloc(const float *logits, int32_t rows, int32_t n_vocab, int64_t ld, int32_t *out,
+                        void *stream);
+
 /* Test-only: the tile configuration of every later GEMM launch in this
  * process (all handles).  tile: -1 automatic (the default, or the
  * WENC_GEMM_TILE environment variable when set), 0 = 128 x 128 tiles,

@@ -22,12 +22,21 @@
 // A row of at most 2048 logits is finished in pass 1.  The work is bound by
 // reading the logits once (HBM), and at one decode step's size by launch
 // latency.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace wk {
 
 namespace {
+
+// Chunk keys of the allocation-free entry point (wenc_argmax_noalloc): one
+// array per device, part of the code object, so the call needs no device
+// allocation.  Host code must not pass the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): static_scratch() looks up its
+// device address once per device and every launch uses that.
+static __device__ __align__(256) uint64_t scratch[ARGMAX_STATIC_KEYS];
 
 constexpr int AM_THREADS = 256;
 constexpr int AM_PER_LANE = 8;
@@ -105,6 +114,25 @@ amax_merge(const uint64_t *__restrict__ part, int nc, int32_t *__restrict__ out)
 }  // namespace
 
 int argmax_chunks(int n_vocab) { return int((int64_t(n_vocab) + AM_CHUNK - 1) / AM_CHUNK); }
+
+hipError_t static_scratch(uint64_t **keys) {
+    static std::mutex mu;
+    static uint64_t *addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        // with `dev` current: each device holds its own copy of the array
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = static_cast<uint64_t *>(p);
+    }
+    *keys = addr[dev];
+    return hipSuccess;
+}
 
 const char *argmax_check(int rows, int n_vocab, int64_t ld) {
     if (rows < 0) return "argmax: rows must be >= 0";

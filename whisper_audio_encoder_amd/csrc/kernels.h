@@ -61,6 +61,11 @@ hipError_t launch_xattn(const uint16_t *q, const uint16_t *xk, const uint16_t *x
 // [rows]; part: workspace of rows * argmax_chunks(n_vocab) keys (unused when
 // that is one chunk per row).
 int argmax_chunks(int n_vocab);
+// The allocation-free variant's chunk keys: a file-scope device array of
+// ARGMAX_STATIC_KEYS keys (1 MiB) per device.  static_scratch() gives its
+// address on the current device (looked up on the first call per device).
+constexpr int64_t ARGMAX_STATIC_KEYS = int64_t(1) << 17;
+hipError_t static_scratch(uint64_t **keys);
 const char *argmax_check(int rows, int n_vocab, int64_t ld);
 hipError_t launch_argmax(const float *logits, int rows, int n_vocab, int64_t ld, uint64_t *part, int32_t *out,
                          hipStream_t s);

@@ -22,16 +22,16 @@
 
 namespace {
 
-thread_local std::string g_err;
+// Message of the last failure in this thread (a fixed buffer: reporting a
+// failure of a handle-less call allocates nothing).
+thread_local char g_err[512];
 
 int fail(std::string *dst, int code, const char *fmt, ...) {
-    char buf[512];
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
     va_end(ap);
-    if (dst) *dst = buf;
-    g_err = buf;
+    if (dst) *dst = g_err;
     return code;
 }
 
@@ -912,7 +912,34 @@ void wenc_destroy(wenc_t *h) {
 
 const char *wenc_last_error(const wenc_t *h) {
     if (h) return h->err.c_str();
-    return g_err.c_str();
+    return g_err;
+}
+
+int wenc_argmax_noalloc(const float *logits, int32_t rows, int32_t n_vocab, int64_t ld, int32_t *out, void *stream) {
+    if (const char *m = wk::argmax_check(rows, n_vocab, ld)) return fail(nullptr, WENC_EINVAL, "wenc_argmax_noalloc: %s", m);
+    const int64_t nc = wk::argmax_chunks(n_vocab);
+    if (nc > 1 && nc > wk::ARGMAX_STATIC_KEYS)
+        return fail(nullptr, WENC_EINVAL,
+                    "wenc_argmax_noalloc: n_vocab %d needs %lld chunk keys per row, beyond the static scratch of %lld "
+                    "(n_vocab <= %lld)",
+                    n_vocab, (long long)nc, (long long)wk::ARGMAX_STATIC_KEYS, (long long)wk::ARGMAX_STATIC_KEYS * 2048);
+    if (rows == 0) return WENC_OK;
+    if (!logits || !out) return fail(nullptr, WENC_EINVAL, "wenc_argmax_noalloc: null pointer");
+    if (misaligned(logits, 4) || misaligned(out, 4))
+        return fail(nullptr, WENC_EINVAL, "wenc_argmax_noalloc: logits and out must be 4-byte aligned");
+    uint64_t *part = nullptr;
+    hipError_t e = wk::static_scratch(&part);
+    if (e != hipSuccess) return fail(nullptr, WENC_EHIP, "wenc_argmax_noalloc: scratch address: %s", hipGetErrorString(e));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // rows in passes of what the scratch holds (each pass's keys are all
+    // written by its first kernel before its second reads them)
+    const int64_t cap = nc > 1 ? std::min<int64_t>(wk::ARGMAX_STATIC_KEYS / nc, rows) : rows;
+    for (int64_t r0 = 0; r0 < rows; r0 += cap) {
+        const int nr = int(std::min<int64_t>(cap, rows - r0));
+        e = wk::launch_argmax(logits + r0 * ld, nr, n_vocab, ld, part, out + r0, st);
+        if (e != hipSuccess) return fail(nullptr, WENC_EHIP, "wenc_argmax_noalloc: launch: %s", hipGetErrorString(e));
+    }
+    return WENC_OK;
 }
 
 int wenc_k_layernorm(const float *x, const float *gamma, const float *beta, void *y, int32_t rows, int32_t d, float eps,

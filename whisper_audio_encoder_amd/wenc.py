@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
     L.wenc_k_gemm_plan.restype = ctypes.c_int
     L.wenc_argmax.argtypes = [vp, vp, i32, i32, ctypes.c_int64, vp, vp]
     L.wenc_argmax.restype = ctypes.c_int
+    L.wenc_argmax_noalloc.argtypes = [vp, i32, i32, ctypes.c_int64, vp, vp]
+    L.wenc_argmax_noalloc.restype = ctypes.c_int
     L.wenc_prepare_cross.restype = ctypes.c_int
     L.wenc_log_mel.argtypes = [vp, vp, i32, vp, vp]
     L.wenc_log_mel.restype = ctypes.c_int
@@ -210,6 +212,11 @@ def wenc_k_gemm_plan(M: int, N: int, cus: int = 256, tile: int = -1, split: int 
 
 def wenc_argmax(h, logits: torch.Tensor, rows: int, n_vocab: int, ld: int, out: torch.Tensor, stream=None) -> None:
     _check(lib().wenc_argmax(h, _ptr(logits), rows, n_vocab, ld, _ptr(out), _stream(stream)), h)
+
+
+def wenc_argmax_noalloc(logits: torch.Tensor, rows: int, n_vocab: int, ld: int, out: torch.Tensor,
+                        stream=None) -> None:
+    _check(lib().wenc_argmax_noalloc(_ptr(logits), rows, n_vocab, ld, _ptr(out), _stream(stream)))
 
 
 def wenc_forward_tap(h, mel: torch.Tensor, batch: int, tap: int, dst: torch.Tensor, stream=None) -> None:
