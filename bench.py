@@ -318,35 +318,24 @@ def run_workload(name, a, with_cpu):
     n_ctx = a.n_ctx
     stream = torch.cuda.current_stream()
 
-    # warm-up: the first forward loads the code objects; the rest run with
-    # events around every launch, which finds the dominant kernel
-    enc.forward(mel_d, out, n_ctx=n_ctx)
-    torch.cuda.synchronize()
-    n_warm = max(a.warmup - 1, 1)
-    wenc.wenc_profile(enc.h, (1 << wenc.N_SITES) - 1)
-    for _ in range(n_warm):
-        enc.forward(mel_d, out, n_ctx=n_ctx)
-    torch.cuda.synchronize()
-    warm = wenc.wenc_profile_read(enc.h)
-    dominant = max(wenc.SITES, key=lambda s: warm[s][0])
-    total_warm = sum(v[0] for v in warm.values()) or 1.0
-    log("[bench] per-site share of kernel time (warm-up): " +
-        ", ".join(f"{s} {100 * warm[s][0] / total_warm:.1f}%" for s in wenc.SITES if warm[s][1]))
+    def timed(e, steps):
+        """ms per forward over `steps` forwards, events on the caller's stream."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            e.forward(mel_d, out, n_ctx=n_ctx)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
 
-    # timed region: events only around the dominant kernel's launches
-    wenc.wenc_profile(enc.h, 1 << wenc.SITES.index(dominant))
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(a.steps):
+    # warm-up (the first forward loads the code objects), then the timed
+    # region: the forward as a caller runs it, no events inside
+    for _ in range(max(a.warmup, 1)):
         enc.forward(mel_d, out, n_ctx=n_ctx)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = timed(enc, a.steps)
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / a.steps
-    prof = wenc.wenc_profile_read(enc.h)
-    wenc.wenc_profile(enc.h, 0)
     log(f"[bench] {name}: {a.steps} steps: {ms:.3f} ms/step (wall {1e3 * wall / a.steps:.3f} ms/step)")
     # per-call times (median, minimum) from events around each forward
     per_call = []
@@ -361,12 +350,43 @@ def run_workload(name, a, with_cpu):
     graph = time_graph(enc, mel_d, out, n_ctx, a.steps)
     log(f"[bench] {name}: hipGraph replay: {graph['ms_per_step']:.3f} ms/step")
 
+    # The kernels' own rates.  The forward above splits its windows over two
+    # streams, so kernels of different sites overlap and no launch's time
+    # is its own.  A second handle runs the same forward with every launch on
+    # the caller's stream (WENC_SPLIT_STREAMS=1): its warm-up, with events
+    # around every launch, finds the dominant site; its timed steps, with
+    # events around that site's launches only, give the roofline.
+    saved = os.environ.get("WENC_SPLIT_STREAMS")
+    os.environ["WENC_SPLIT_STREAMS"] = "1"
+    try:
+        enc1 = wenc.Encoder(model, blob, max_batch=B)
+    finally:
+        if saved is None:
+            del os.environ["WENC_SPLIT_STREAMS"]
+        else:
+            os.environ["WENC_SPLIT_STREAMS"] = saved
+    enc1.forward(mel_d, out, n_ctx=n_ctx)
+    n_warm = max(a.warmup - 1, 1)
+    wenc.wenc_profile(enc1.h, (1 << wenc.N_SITES) - 1)
+    timed(enc1, n_warm)
+    warm = wenc.wenc_profile_read(enc1.h)
+    dominant = max(wenc.SITES, key=lambda s: warm[s][0])
+    total_warm = sum(v[0] for v in warm.values()) or 1.0
+    log("[bench] per-site share of kernel time (one stream, warm-up): " +
+        ", ".join(f"{s} {100 * warm[s][0] / total_warm:.1f}%" for s in wenc.SITES if warm[s][1]))
+    wenc.wenc_profile(enc1.h, 1 << wenc.SITES.index(dominant))
+    ms1 = timed(enc1, a.steps)
+    prof = wenc.wenc_profile_read(enc1.h)
+    wenc.wenc_profile(enc1.h, 0)
+    enc1.close()
+    log(f"[bench] {name}: one stream: {ms1:.3f} ms/step")
+
     flops = cfg.flops_per_window() * B
     tflops = flops / (ms * 1e-3) / 1e12
-    # The dominant site over the whole batch: its algorithmic work per
-    # application (all windows) over the wall time it ran per application
-    # (the library's events give the union of its launches' intervals, so
-    # the launches of the split forward's streams, which overlap, count once).
+    # The dominant site over the whole batch, on one stream: its algorithmic
+    # work per application (all windows) over its time per application (the
+    # library's events bracket each launch; a site launched as two kernels,
+    # fc1's two tile sizes, counts both).
     kind, work = site_work(cfg, B)[dominant]
     d_ms, d_n = prof[dominant]
     per_step = site_launches_per_step(cfg, dominant)
@@ -381,6 +401,8 @@ def run_workload(name, a, with_cpu):
     roof["avg_launch_ms"] = avg_s * 1e3
     roof["launches"] = d_n
     roof["applications"] = a.steps * per_step
+    roof["measured_on"] = ("one stream: the timed steps of a second handle whose forward keeps every launch "
+                           "on the caller's stream")
 
     frontend = time_frontend(enc, model, B, a.steps) if a.frontend else None
     cross = time_cross(enc, model, out, a.cross, a.steps) if a.cross else None
@@ -403,6 +425,7 @@ def run_workload(name, a, with_cpu):
         "pct_fp16_peak": 100.0 * tflops / PEAK_F16_TFLOPS,
         "per_call_ms": {"median": call_ms[len(call_ms) // 2], "min": call_ms[0], "calls": len(call_ms)},
         "graph_replay": graph,
+        "one_stream": {"ms_per_step": ms1, "value": B / (ms1 * 1e-3)},
         "site_ms_per_step": {s: warm[s][0] / n_warm for s in wenc.SITES if warm[s][1]},
         "roofline": roof,
         "cpu_baseline": cpu,

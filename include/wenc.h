@@ -316,14 +316,17 @@ int wenc_argmax_noalloc(const float *logits, int32_t rows, int32_t n_vocab, int6
  * with an old split).  Returns WENC_EINVAL for values out of range. */
 int wenc_k_gemm_mode(int32_t tile, int32_t split);
 
-/* Test-only, host logic (no device work): the tile plan wenc_k_gemm would use
+/* Test-only, host logic (no device work): the tile plan a GEMM launch uses
  * for M output rows (after the QKV epilogue's padding to 16 keys per item)
- * and N columns on `cus` compute units, with tile and split as in
- * wenc_k_gemm_mode (tile -1 = automatic, ignoring the environment).  Returns
+ * and N columns on a device of `cus` compute units, with tile and split as
+ * in wenc_k_gemm_mode (tile -1 = automatic, ignoring the environment), when
+ * `streams` streams run such launches side by side (1 for wenc_k_gemm and a
+ * forward kept on one stream, 2 for wenc_forward's default split).  Returns
  * 0 = all 128 x 128 tiles, 1 = all 256 x 256 tiles, 2 = 256 x 256 tiles for
  * rows [0, *big_rows) and 128 x 128 for the rest; *big_rows is M for 1 and
  * 0 for 0.  WENC_EINVAL for values out of range. */
-int wenc_k_gemm_plan(int32_t M, int32_t N, int32_t cus, int32_t tile, int32_t split, int32_t *big_rows);
+int wenc_k_gemm_plan(int32_t M, int32_t N, int32_t cus, int32_t tile, int32_t split, int32_t streams,
+                     int32_t *big_rows);
 
 /* Non-causal attention per (batch, head) (kernels.nu, wk_attn with causal 0):
  *   ao[b][t][h*64 + e] = sum_u softmax_u(q[b][h][t] . k[b][h][u]) * v[b][h][u][e]

@@ -36,6 +36,39 @@ def test_plan_on_encoder_shapes(name):
     assert wenc.wenc_k_gemm_plan(M, N, 256) == want
 
 
+# the same projections for one half of the batch when wenc_forward runs the
+# two halves on two streams side by side (measured fastest that way)
+SHARED_PLANS = {
+    "c4 fc1": ((12000, 5120), (BIG, 12000)),
+    "c4 out_proj / fc2": ((12000, 1280), (BIG, 12000)),
+    "c3 out_proj / fc2": ((12000, 768), (BIG, 12000)),
+    "c3 qkv": ((8 * 1504, 2304), (BIG, 8 * 1504)),
+    "c2 out_proj / fc2 / conv2": ((6000, 512), (SMALL, 0)),
+    "c2 conv1": ((12000, 512), (SMALL, 0)),
+    "c2 qkv": ((4 * 1504, 1536), (BIG, 4 * 1504)),
+    "c2 fc1": ((6000, 2048), (BIG, 6000)),
+}
+
+
+@pytest.mark.parametrize("name", list(SHARED_PLANS))
+def test_plan_on_two_streams(name):
+    (M, N), want = SHARED_PLANS[name]
+    assert wenc.wenc_k_gemm_plan(M, N, 256, streams=2) == want
+
+
+@pytest.mark.parametrize("streams", [2, 3, 4])
+def test_shared_plan_invariants(streams):
+    for cus in (80, 256, 304):
+        for N in (64, 512, 768, 1280, 2304, 5120):
+            for M in range(1, 40000, 1499):
+                kind, rows = wenc.wenc_k_gemm_plan(M, N, cus, streams=streams)
+                tm, tn = math.ceil(M / 256), math.ceil(N / 256)
+                # whole launches on one tile size, big from 0.75 tiles per unit of the CU share on
+                assert kind in (SMALL, BIG), (M, N, cus, kind)
+                assert (kind == SMALL) == (4 * tm * tn < 3 * (cus // streams)), (M, N, cus, streams)
+                assert rows == (M if kind == BIG else 0)
+
+
 def test_forced_and_unsplit_plans():
     for M, N in ((24000, 5120), (1500, 384), (1, 64), (100000, 768)):
         assert wenc.wenc_k_gemm_plan(M, N, 256, tile=1) == (BIG, M)
@@ -64,6 +97,6 @@ def test_plan_invariants(cus):
 
 def test_plan_rejects_bad_arguments():
     for args in ((0, 64, 256, -1, 1), (64, 0, 256, -1, 1), (64, 64, 0, -1, 1), (64, 64, 256, 2, 1),
-                 (64, 64, 256, -2, 1), (64, 64, 256, -1, 2)):
+                 (64, 64, 256, -2, 1), (64, 64, 256, -1, 2), (64, 64, 256, -1, 1, 0)):
         with pytest.raises(ValueError):
             wenc.wenc_k_gemm_plan(*args)

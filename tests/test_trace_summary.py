@@ -1,0 +1,30 @@
+"""The rocprofv3 trace summariser (host logic): kernel-name to site mapping
+and the even split of overlapping kernels' time."""
+import pytest
+
+from whisper_audio_encoder_amd import trace_summary as ts
+
+
+def test_site_of_kernel_names():
+    g = "void wk::(anonymous namespace)::gemm_kernel<256, 256, 128, 64, 8, {e}, {t}>(wk::(anonymous namespace)::GemmP)"
+    assert ts.site_of(g.format(e=0, t=1)) == "fc1"
+    assert ts.site_of(g.format(e=0, t=0)) == "conv1"
+    assert ts.site_of(g.format(e=2, t=0)) == "oproj"
+    assert ts.site_of(g.format(e=2, t=1)) == "fc2"
+    assert ts.site_of(g.format(e=3, t=0)) == "qkv"
+    assert ts.site_of("_ZN2wk12_GLOBAL__N_111attn_kernelEPKDF16_S2_S2_PDF16_iii") == "attn"
+    assert ts.site_of("void wk::(anonymous namespace)::ln_kernel<5, false>(float const*)") == "ln"
+    assert ts.site_of("void wk::(anonymous namespace)::ln_kernel<5, true>(float const*)") == "lnf"
+    assert ts.site_of("__amd_rocclr_copyBuffer") is None
+
+
+def test_fair_share_splits_overlaps_evenly():
+    # a: [0, 10), b: [5, 15), c: [20, 30) -> a 5 + 2.5, b 2.5 + 5, c 10; busy 25
+    share, busy = ts.fair_share_ns([(0, 10, "a"), (5, 15, "b"), (20, 30, "c")])
+    assert busy == 25
+    assert share["a"] == pytest.approx(7.5) and share["b"] == pytest.approx(7.5) and share["c"] == pytest.approx(10)
+    # sequential kernels keep their own durations; the shares add up to the busy time
+    share, busy = ts.fair_share_ns([(0, 4, "x"), (4, 9, "y"), (9, 10, "x")])
+    assert (share["x"], share["y"], busy) == (5, 5, 10)
+    share, busy = ts.fair_share_ns([(0, 12, "x"), (2, 4, "y"), (3, 8, "z")])
+    assert sum(share.values()) == pytest.approx(busy) == 12

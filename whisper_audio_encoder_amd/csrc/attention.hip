@@ -32,6 +32,9 @@ namespace {
 
 constexpr int QT = 128;  // queries per workgroup
 constexpr int KT = 64;   // keys per tile
+// s_waitcnt immediate with vmcnt = 0 and the other counters left alone
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int WAIT_VMCNT0 = 0x0f70;
 
 // LDS chunk swizzle of a 128-byte row: conflict-free 16-byte reads for the 16
 // lanes the LDS serves per cycle across its 64 banks.
@@ -101,6 +104,13 @@ attn_kernel(const f16 *__restrict__ q, const f16 *__restrict__ k, const f16 *__r
         else
             qf[kk] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
+
+    // Wait for the Q loads here, with a wait the compiler sees: its own
+    // bookkeeping would otherwise place that wait inside the key loop, where
+    // the hardware counter also holds the next key tile's transfers (issued
+    // as inline assembly, invisible to the compiler), and every step would
+    // stall until most of them had landed.
+    __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);
 
     // Tile transfers: each wave moves rows 16 wave .. 16 wave + 15 of the K
     // tile and of the V^T tile (two 8-row groups each).  Lane i lands at row

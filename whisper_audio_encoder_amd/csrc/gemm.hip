@@ -283,16 +283,22 @@ gemm_kernel(const GemmP p) {
     // Accumulator (i, j) is the 16 x 16 block of rows 16 i and columns 16 j of
     // the wave's tile; its register r holds row (lane & 15) and column
     // 4 (lane >> 4) + r.  Every accumulator starts at its column's bias, so
-    // the epilogues add none.
+    // the epilogues add none.  The bias loads are issued first, as inline
+    // assembly like the direct loads, and the prologue's own wait covers
+    // them (transfers complete in issue order).  Issued as ordinary loads,
+    // they would make the compiler wait for them just before the first
+    // step, where the hardware counter also holds the direct loads of the
+    // next two steps (invisible to it), so the first step would not start
+    // until those had landed.
     const int hh = lane >> 4;
-    f32x4 acc[TM][TN];
+    f32x4 bias[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int n = n0 + wn * WN + j * 16 + 4 * hh;
-        const f32x4 b = n < p.N ? ld4(p.bias + n) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < TM; ++i) acc[i][j] = b;
+        const float *bp = p.bias + min(n, p.N - 4);  // a column past N loads column N - 4 and is zeroed below
+        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(bias[j]) : "v"(bp) : "memory");
     }
+    f32x4 acc[TM][TN];
 
     // Fragment reads (v_mfma_f32_16x16x32_f16 operands): lane supplies row
     // (lane & 15) of a 16-row block and k values 8 (lane >> 4) .. +7 of the
@@ -363,11 +369,22 @@ gemm_kernel(const GemmP p) {
     const f16 *A0 = smem0, *A1 = smem1, *A2 = smemA2, *W0 = smem0 + ASZ, *W1 = smem1 + ASZ;
     issueW(0, lw0);
     issueA(0, la0);
-    if (nk > 1) {
+    if (nk > 1 && wave < LW) {
         issueA(1, la1);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(AG) : "memory");
     } else {
+        // (a wave that issues no direct loads has only the bias loads out)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    // the bias registers are valid from here: nothing reads them earlier
+#pragma unroll
+    for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(bias[j]));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * WN + j * 16 + 4 * hh;
+        const f32x4 b = n < p.N ? bias[j] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < TM; ++i) acc[i][j] = b;
     }
     __syncthreads();
     if (nk > 1) issueW(1, lw1);
@@ -712,7 +729,7 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag, int cu_d
         p.t_div = make_divu(tp);
     }
     const int tile = tile_mode().tile.load(), split = tile_mode().split.load();
-    const GemmPlan plan = gemm_plan(p.M, p.N, std::max(1L, cu_count() / std::max(cu_div, 1)), tile == 0 || tile == 1 ? tile : -1, split);
+    const GemmPlan plan = gemm_plan(p.M, p.N, cu_count(), tile == 0 || tile == 1 ? tile : -1, split, std::max(cu_div, 1));
     if (plan.kind == GEMM_PLAN_SMALL) return launch_tagged<128, 128, 64, 64, 4>(p, a.epilogue, tag, s);
     if (plan.kind == GEMM_PLAN_BIG) return launch_tagged<256, 256, 128, 64, 8>(p, a.epilogue, tag, s);
     GemmP big = p;
@@ -724,13 +741,24 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag, int cu_d
     return launch_tagged<128, 128, 64, 64, 4>(tail, a.epilogue, tag, s);
 }
 
-GemmPlan gemm_plan(int M, int N, long cus, int tile, int split) {
+GemmPlan gemm_plan(int M, int N, long cus, int tile, int split, int streams) {
     if (tile == 1) return {GEMM_PLAN_BIG, M};
     if (tile == 0) return {GEMM_PLAN_SMALL, 0};
+    const long tn_big = (N + 255) / 256, tm_big = (long(M) + 255) / 256;
+    if (streams > 1) {
+        // Launches of a forward split over several streams run side by side,
+        // each with about cus / streams compute units: the 256 x 256 tiles
+        // from 0.75 tiles per such unit on, on whole launches (measured on
+        // two streams: on c3's 24000-row projections, whose halves have 141
+        // such tiles at N = 768, they beat 128 x 128 tiles by 7% of a
+        // step; carving the last tile rows into small tiles, which pays on
+        // one stream, cost 1-7%).
+        const long share = std::max(1L, cus / streams);
+        return 4 * tm_big * tn_big < 3 * share ? GemmPlan{GEMM_PLAN_SMALL, 0} : GemmPlan{GEMM_PLAN_BIG, M};
+    }
     // 256 x 256 tiles when they fill the CUs at least 1.75 times over
     // (measured on 256 CUs: on 24000 x 768 x {768, 3072}, 282 such tiles,
     // the 128 x 128 tiles at two workgroups per CU are 10-20% faster).
-    const long tn_big = (N + 255) / 256, tm_big = (long(M) + 255) / 256;
     if (4 * tm_big * tn_big < 7 * cus) return {GEMM_PLAN_SMALL, 0};
     // The 256 x 256 kernel runs one tile per CU at a time, so a tile count
     // just past a multiple of the CU count leaves most CUs idle in the last

@@ -16,7 +16,8 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag = 0, int 
 // Tile configuration of later launches (see wenc_k_gemm_mode); -1 if out of range.
 int gemm_mode(int tile, int split);
 // Tile plan of one GEMM launch over M rows (as the kernel sees them) and N
-// columns on `cus` compute units: all 128 x 128 tiles, all 256 x 256, or
+// columns on a device of `cus` compute units shared by `streams` streams
+// running launches side by side: all 128 x 128 tiles, all 256 x 256, or
 // 256 x 256 for rows [0, big_rows) and 128 x 128 for the rest.  tile: -1
 // chooses, 0 / 1 force 128 / 256; split 0 keeps one tile size.
 enum { GEMM_PLAN_SMALL = 0, GEMM_PLAN_BIG = 1, GEMM_PLAN_SPLIT = 2 };
@@ -24,7 +25,7 @@ struct GemmPlan {
     int kind;
     int big_rows;
 };
-GemmPlan gemm_plan(int M, int N, long cus, int tile, int split);
+GemmPlan gemm_plan(int M, int N, long cus, int tile, int split, int streams);
 
 const char *attention_check(int batch, int n_head, int T, int ldvt);
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, uint16_t *ao,

@@ -962,10 +962,12 @@ int wenc_k_gemm_mode(int32_t tile, int32_t split) {
     return WENC_OK;
 }
 
-int wenc_k_gemm_plan(int32_t M, int32_t N, int32_t cus, int32_t tile, int32_t split, int32_t *big_rows) {
-    if (M < 1 || N < 1 || cus < 1 || tile < -1 || tile > 1 || split < 0 || split > 1 || !big_rows)
-        return fail(nullptr, WENC_EINVAL, "gemm plan: need M, N, cus >= 1, tile in [-1, 1], split in [0, 1], big_rows");
-    const wk::GemmPlan p = wk::gemm_plan(M, N, cus, tile, split);
+int wenc_k_gemm_plan(int32_t M, int32_t N, int32_t cus, int32_t tile, int32_t split, int32_t streams,
+                     int32_t *big_rows) {
+    if (M < 1 || N < 1 || cus < 1 || tile < -1 || tile > 1 || split < 0 || split > 1 || streams < 1 || !big_rows)
+        return fail(nullptr, WENC_EINVAL,
+                    "gemm plan: need M, N, cus, streams >= 1, tile in [-1, 1], split in [0, 1], big_rows");
+    const wk::GemmPlan p = wk::gemm_plan(M, N, cus, tile, split, streams);
     *big_rows = p.big_rows;
     return p.kind;
 }

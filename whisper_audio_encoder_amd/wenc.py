@@ -87,7 +87,7 @@ def lib() -> ctypes.CDLL:
     L.wenc_prepare_cross.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     L.wenc_cross_attend.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
     L.wenc_cross_attend.restype = ctypes.c_int
-    L.wenc_k_gemm_plan.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i32)]
+    L.wenc_k_gemm_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32)]
     L.wenc_k_gemm_plan.restype = ctypes.c_int
     L.wenc_argmax.argtypes = [vp, vp, i32, i32, ctypes.c_int64, vp, vp]
     L.wenc_argmax.restype = ctypes.c_int
@@ -201,10 +201,11 @@ def wenc_cross_attend(h, q: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, ba
     _check(lib().wenc_cross_attend(h, _ptr(q), _ptr(xk), _ptr(xv), batch, n_q, n_ctx, _ptr(out), _stream(stream)), h)
 
 
-def wenc_k_gemm_plan(M: int, N: int, cus: int = 256, tile: int = -1, split: int = 1) -> tuple[int, int]:
+def wenc_k_gemm_plan(M: int, N: int, cus: int = 256, tile: int = -1, split: int = 1,
+                     streams: int = 1) -> tuple[int, int]:
     """Host-side tile plan of a GEMM launch: (kind, big_rows), see wenc.h."""
     rows = ctypes.c_int32()
-    kind = lib().wenc_k_gemm_plan(M, N, cus, tile, split, ctypes.byref(rows))
+    kind = lib().wenc_k_gemm_plan(M, N, cus, tile, split, streams, ctypes.byref(rows))
     if kind < 0:
         raise ValueError(f"wenc_k_gemm_plan: {wenc_last_error()}")
     return kind, rows.value
