@@ -149,26 +149,19 @@ def device_peak():
 
 
 def time_graph(enc, mel_d, out, n_ctx, steps):
-    """The same step captured once into a hipGraph (torch.cuda.CUDAGraph on a
-    default-priority side stream) and replayed: what a caller that replays
-    the forward pays, launch overhead excluded."""
+    """The same step through the library's record-once / replay entry point
+    (wenc_forward_graph: the forward recorded into a hipGraph on the first
+    call, launched as one graph afterwards): what a caller that replays the
+    forward pays, launch overhead excluded."""
     import torch
-    g = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        enc.forward(mel_d, out, n_ctx=n_ctx)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        enc.forward(mel_d, out, n_ctx=n_ctx)
-    g.replay()
+    enc.forward_graph(mel_d, out, n_ctx=n_ctx)  # records
+    enc.forward_graph(mel_d, out, n_ctx=n_ctx)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(steps):
-        g.replay()
+        enc.forward_graph(mel_d, out, n_ctx=n_ctx)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
@@ -177,12 +170,11 @@ def time_graph(enc, mel_d, out, n_ctx, steps):
     for _ in range(max(steps // 2, 3)):
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         c0.record(stream)
-        g.replay()
+        enc.forward_graph(mel_d, out, n_ctx=n_ctx)
         c1.record(stream)
         per.append((c0, c1))
     torch.cuda.synchronize()
     call_ms = sorted(c0.elapsed_time(c1) for c0, c1 in per)
-    del g
     return {"ms_per_step": ms, "value": mel_d.shape[0] / (ms * 1e-3),
             "per_call_ms": {"median": call_ms[len(call_ms) // 2], "min": call_ms[0], "calls": len(call_ms)}}
 

@@ -130,6 +130,22 @@ int wenc_forward(wenc_t *h, const float *mel, int32_t batch, float *out, void *s
  * shorter).  Enqueued on `stream`; no host synchronisation. */
 int wenc_forward_ctx(wenc_t *h, const float *mel, int32_t batch, int32_t n_ctx, float *out, void *stream);
 
+/* Record once, replay: the same forward as wenc_forward_ctx (n_ctx equal to
+ * the configured one is a full window), enqueued as one recorded HIP graph
+ * (whisper README, "Implementation notes": the encoder is recorded once
+ * and replayed).  The first call with a given (mel, out, batch, n_ctx)
+ * records every launch of the forward, chunks and both stream groups
+ * included, into a graph on a stream the handle owns and instantiates it;
+ * that call and every later call with the same four values launch the
+ * graph on `stream`.  A call with any other value records anew and
+ * replaces the kept graph.  The graph refers to the handle's weight arena
+ * and scratch by address: it stays valid across wenc_load (which rewrites
+ * the arena in place) and is released by wenc_destroy.  Same arguments,
+ * alignment and errors as wenc_forward_ctx; WENC_ESTATE while per-launch
+ * profiling (wenc_profile) or WENC_DEBUG_SYNC is on, which a graph cannot
+ * hold.  One stream at a time per handle, as for every forward. */
+int wenc_forward_graph(wenc_t *h, const float *mel, int32_t batch, int32_t n_ctx, float *out, void *stream);
+
 /* Release the handle and every device allocation it owns (whisper 0.9.0
  * API page, wh_close, and the Whisper struct's list of every device
  * allocation kept for the free).  NULL-safe.  Synchronises the device first

@@ -238,6 +238,13 @@ struct wenc {
     hipStream_t aux[MAX_PARTS - 1] = {};
     hipEvent_t ev_fork = nullptr, ev_join[MAX_PARTS - 1] = {};
     int n_parts = 2;  // a chunk's windows are split over this many streams
+    // Recorded forward (wenc_forward_graph): the graph of one forward over
+    // (g_mel, g_out, g_batch, g_nctx), recorded on the capture stream.
+    hipStream_t cap = nullptr;
+    hipGraphExec_t gexec = nullptr;
+    const float *g_mel = nullptr;
+    float *g_out = nullptr;
+    int g_batch = 0, g_nctx = 0;
 
     template <class T>
     T *W(size_t off) const { return reinterpret_cast<T *>(warena + off); }
@@ -508,6 +515,8 @@ static void release(wenc *h) {
         (void)hipEventDestroy(r.e1);
     }
     for (auto e : h->event_pool) (void)hipEventDestroy(e);
+    if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
+    if (h->cap) (void)hipStreamDestroy(h->cap);
     if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
     for (int i = 0; i + 1 < wenc::MAX_PARTS; ++i) {
         if (h->ev_join[i]) (void)hipEventDestroy(h->ev_join[i]);
@@ -570,6 +579,7 @@ int wenc_create(const wenc_config *cfg, wenc_t **out) {
     };
     int rc = WENC_OK;
     e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking);
     for (int i = 0; i + 1 < h->n_parts && e == hipSuccess; ++i) {
         e = hipStreamCreateWithFlags(&h->aux[i], hipStreamNonBlocking);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_join[i], hipEventDisableTiming);
@@ -678,6 +688,18 @@ int wenc_load(wenc_t *h, const void *blob, size_t nbytes) {
     return WENC_OK;
 }
 
+// Every chunk of a checked forward, in order, on stream st.
+static int enqueue_forward(wenc_t *h, const float *mel, int32_t batch, int32_t n_ctx, float *out, hipStream_t st) {
+    const wenc_config &c = h->cfg;
+    const int cap = h->chunk_cap(n_ctx);
+    for (int b0 = 0; b0 < batch; b0 += cap) {
+        const int nb = batch - b0 < cap ? batch - b0 : cap;
+        WENC_TRY(h->forward_chunk(mel + size_t(b0) * 2 * n_ctx * c.n_mels, nb, n_ctx,
+                                  out + size_t(b0) * n_ctx * c.d_model, st, -1, nullptr));
+    }
+    return WENC_OK;
+}
+
 static int forward_impl(wenc_t *h, const float *mel, int32_t batch, int32_t n_ctx, float *out, void *stream, int tap,
                         void *tap_dst) {
     if (!h) return fail(nullptr, WENC_EINVAL, "wenc_forward: handle is NULL");
@@ -700,13 +722,7 @@ static int forward_impl(wenc_t *h, const float *mel, int32_t batch, int32_t n_ct
     }
     if (!out) return fail(&h->err, WENC_EINVAL, "wenc_forward: out is NULL");
     if (misaligned(out, 16)) return fail(&h->err, WENC_EINVAL, "wenc_forward: out must be 16-byte aligned");
-    const int cap = h->chunk_cap(n_ctx);
-    for (int b0 = 0; b0 < batch; b0 += cap) {
-        const int nb = batch - b0 < cap ? batch - b0 : cap;
-        WENC_TRY(h->forward_chunk(mel + size_t(b0) * 2 * n_ctx * c.n_mels, nb, n_ctx,
-                                  out + size_t(b0) * n_ctx * c.d_model, st, -1, nullptr));
-    }
-    return WENC_OK;
+    return enqueue_forward(h, mel, batch, n_ctx, out, st);
 }
 
 int wenc_forward(wenc_t *h, const float *mel, int32_t batch, float *out, void *stream) {
@@ -715,6 +731,57 @@ int wenc_forward(wenc_t *h, const float *mel, int32_t batch, float *out, void *s
 
 int wenc_forward_ctx(wenc_t *h, const float *mel, int32_t batch, int32_t n_ctx, float *out, void *stream) {
     return forward_impl(h, mel, batch, n_ctx, out, stream, -1, nullptr);
+}
+
+int wenc_forward_graph(wenc_t *h, const float *mel, int32_t batch, int32_t n_ctx, float *out, void *stream) {
+    if (!h) return fail(nullptr, WENC_EINVAL, "wenc_forward_graph: handle is NULL");
+    if (!h->loaded) return fail(&h->err, WENC_ESTATE, "wenc_forward_graph: no weights loaded (call wenc_load first)");
+    const wenc_config &c = h->cfg;
+    if (batch < 0) return fail(&h->err, WENC_EINVAL, "wenc_forward_graph: batch %d < 0", batch);
+    if (n_ctx < 1 || n_ctx > c.n_ctx)
+        return fail(&h->err, WENC_EINVAL, "wenc_forward_graph: n_ctx %d outside [1, %d]", n_ctx, c.n_ctx);
+    if (batch == 0) return WENC_OK;
+    if (!mel || !out) return fail(&h->err, WENC_EINVAL, "wenc_forward_graph: mel and out must be non-null");
+    if (misaligned(mel, 16) || misaligned(out, 16))
+        return fail(&h->err, WENC_EINVAL, "wenc_forward_graph: mel and out must be 16-byte aligned");
+    if (h->prof_mask || h->debug_sync)
+        return fail(&h->err, WENC_ESTATE,
+                    "wenc_forward_graph: not while per-launch profiling or WENC_DEBUG_SYNC is on (neither can be "
+                    "recorded into a graph)");
+    hipError_t e = hipSetDevice(h->device);
+    if (e != hipSuccess) return fail(&h->err, WENC_EHIP, "wenc_forward_graph: hipSetDevice: %s", hipGetErrorString(e));
+    if (!h->gexec || h->g_mel != mel || h->g_out != out || h->g_batch != batch || h->g_nctx != n_ctx) {
+        // record the forward once for these buffers and sizes
+        if (h->gexec) {
+            e = hipGraphExecDestroy(h->gexec);
+            h->gexec = nullptr;
+            if (e != hipSuccess)
+                return fail(&h->err, WENC_EHIP, "wenc_forward_graph: releasing the previous graph: %s", hipGetErrorString(e));
+        }
+        e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal);
+        if (e != hipSuccess) return fail(&h->err, WENC_EHIP, "wenc_forward_graph: begin capture: %s", hipGetErrorString(e));
+        const int rc = enqueue_forward(h, mel, batch, n_ctx, out, h->cap);
+        hipGraph_t g = nullptr;
+        e = hipStreamEndCapture(h->cap, &g);
+        if (rc != WENC_OK || e != hipSuccess || !g) {
+            if (g) (void)hipGraphDestroy(g);
+            if (rc != WENC_OK) return rc;
+            return fail(&h->err, WENC_EHIP, "wenc_forward_graph: end capture: %s", hipGetErrorString(e));
+        }
+        e = hipGraphInstantiate(&h->gexec, g, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(g);  // the executable graph keeps what it needs
+        if (e != hipSuccess) {
+            h->gexec = nullptr;
+            return fail(&h->err, WENC_EHIP, "wenc_forward_graph: instantiate: %s", hipGetErrorString(e));
+        }
+        h->g_mel = mel;
+        h->g_out = out;
+        h->g_batch = batch;
+        h->g_nctx = n_ctx;
+    }
+    e = hipGraphLaunch(h->gexec, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(&h->err, WENC_EHIP, "wenc_forward_graph: launch: %s", hipGetErrorString(e));
+    return WENC_OK;
 }
 
 int wenc_forward_tap(wenc_t *h, const float *mel, int32_t batch, int32_t tap, void *dst, void *stream) {

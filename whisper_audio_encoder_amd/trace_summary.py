@@ -82,13 +82,29 @@ def fair_share_ns(intervals):
     return share, busy
 
 
-def summarise(path: str, workload: str, parts: int) -> str:
+def _rows(path: str, region: str):
+    """The trace's kernel dispatches in start order; with region "first" or
+    "second", those before or after the start of the second scratch fill
+    (wenc_create clears a new handle's scratch, so in a bench.py trace the
+    second fill starts the second handle, the one-stream roofline pass)."""
+    with open(path) as fh:
+        rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
+    if region == "all":
+        return rows
+    fills = [int(r["Start_Timestamp"]) for r in rows if "fillBuffer" in r["Kernel_Name"]]
+    if len(fills) < 2:
+        raise SystemExit("the trace holds fewer than two scratch fills: no second handle")
+    cut = fills[1]
+    return [r for r in rows if (int(r["Start_Timestamp"]) < cut) == (region == "first")]
+
+
+def summarise(path: str, workload: str, parts: int, region: str = "all") -> str:
     cfg = CONFIGS[workload]
     per_kernel = defaultdict(list)
     per_site = defaultdict(list)
     intervals = []
-    with open(path) as fh:
-        for row in csv.DictReader(fh):
+    if True:
+        for row in _rows(path, region):
             name = row["Kernel_Name"]
             t0, t1 = int(row["Start_Timestamp"]), int(row["End_Timestamp"])
             per_kernel[name].append(t1 - t0)
@@ -99,7 +115,8 @@ def summarise(path: str, workload: str, parts: int) -> str:
     share, busy = fair_share_ns(intervals)
     total = sum(sum(v) for v in per_kernel.values()) or 1
     forwards = len(per_site.get("lnf", [])) / parts if cfg.final_ln else len(per_site.get("ingest", [])) / parts
-    out = [f"Per kernel ({path.split('/')[-1]}; {forwards:g} forwards of {workload} split over {parts} streams):", "",
+    out = [f"Per kernel ({path.split('/')[-1]}, {region} dispatches; {forwards:g} forwards of {workload} over "
+           f"{parts} stream(s)):", "",
            "| kernel | site | calls | avg us | % of kernel time |", "|---|---|---|---|---|"]
     for name, d in sorted(per_kernel.items(), key=lambda kv: -sum(kv[1])):
         short = re.sub(r"\(.*", "", name.replace("void ", "").replace("wk::(anonymous namespace)::", ""))
@@ -201,6 +218,8 @@ def main(argv=None):
     ap.add_argument("trace", help="kernel_trace.csv, or counter_collection.csv with --util / --traffic")
     ap.add_argument("--workload", default="c4", choices=sorted(CONFIGS))
     ap.add_argument("--parts", type=int, default=2, help="streams a forward's windows are split over")
+    ap.add_argument("--region", default="all", choices=["all", "first", "second"],
+                    help="kernel trace of bench.py: its first handle (the timed forward) or its second (one stream)")
     ap.add_argument("--util", action="store_true", help="the file holds GRBM_GUI_ACTIVE and MFMA-busy counters")
     ap.add_argument("--traffic", nargs=3, metavar=("WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="the file holds FETCH_SIZE; with the WRITE_SIZE run and the copy calibration runs")
@@ -223,7 +242,7 @@ def main(argv=None):
                               "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
                               "hbm_bytes_per_launch": fb + wb}, indent=1))
     else:
-        print(summarise(a.trace, a.workload, a.parts))
+        print(summarise(a.trace, a.workload, a.parts, a.region))
 
 
 if __name__ == "__main__":

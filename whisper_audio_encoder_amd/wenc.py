@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.wenc_log_mel.restype = ctypes.c_int
     L.wenc_forward_ctx.argtypes = [vp, vp, i32, i32, vp, vp]
     L.wenc_forward_ctx.restype = ctypes.c_int
+    L.wenc_forward_graph.argtypes = [vp, vp, i32, i32, vp, vp]
+    L.wenc_forward_graph.restype = ctypes.c_int
     L.wenc_forward_tap.argtypes = [vp, vp, i32, i32, vp, vp]
     L.wenc_forward_tap.restype = ctypes.c_int
     L.wenc_destroy.argtypes = [vp]
@@ -176,6 +178,10 @@ def wenc_forward(h, mel: torch.Tensor, batch: int, out: torch.Tensor, stream=Non
 
 def wenc_forward_ctx(h, mel: torch.Tensor, batch: int, n_ctx: int, out: torch.Tensor, stream=None) -> None:
     _check(lib().wenc_forward_ctx(h, _ptr(mel), batch, n_ctx, _ptr(out), _stream(stream)), h)
+
+
+def wenc_forward_graph(h, mel: torch.Tensor, batch: int, n_ctx: int, out: torch.Tensor, stream=None) -> None:
+    _check(lib().wenc_forward_graph(h, _ptr(mel), batch, n_ctx, _ptr(out), _stream(stream)), h)
 
 
 def wenc_log_mel(h, audio: torch.Tensor, batch: int, mel: torch.Tensor, stream=None) -> None:
@@ -292,6 +298,22 @@ class Encoder:
             wenc_forward(self.h, mel, B, out, stream)
         else:
             wenc_forward_ctx(self.h, mel, B, n_ctx, out, stream)
+        return out
+
+    def forward_graph(self, mel: torch.Tensor, out: torch.Tensor | None = None, stream=None,
+                      n_ctx: int | None = None) -> torch.Tensor:
+        """forward() through the library's recorded graph: recorded on the
+        first call for these buffers and sizes, replayed afterwards."""
+        c = self.cfg
+        T = c.n_ctx if n_ctx is None else n_ctx
+        self._check_mel(mel, 2 * T)
+        B = mel.shape[0]
+        if out is None:
+            out = torch.empty((B, T, c.d_model), dtype=torch.float32, device=mel.device)
+        elif not (out.is_cuda and out.dtype == torch.float32 and out.is_contiguous()
+                  and tuple(out.shape) == (B, T, c.d_model)):
+            raise ValueError(f"out must be a contiguous fp32 device tensor [batch, {T}, d_model]")
+        wenc_forward_graph(self.h, mel, B, T, out, stream)
         return out
 
     def log_mel(self, audio: torch.Tensor, mel: torch.Tensor | None = None, stream=None) -> torch.Tensor:
