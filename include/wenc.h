@@ -355,12 +355,14 @@ int wenc_k_gemm_plan(int32_t M, int32_t N, int32_t cus, int32_t tile, int32_t sp
 int wenc_k_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, uint16_t *ao,
                      int32_t batch, int32_t n_head, int32_t T, int32_t ldvt, void *stream);
 
-/* Per-launch timing of wenc_forward, wenc_prepare_cross and wenc_log_mel
- * with HIP events recorded on the caller's stream around the launches whose
- * site bit is set in `site_mask`
- * (and wenc_cross_attend, wenc_argmax)
- * (bit s = 1 << WENC_SITE_*); 0 turns it off.  Events are read, and cleared,
- * by wenc_profile_read (which synchronises on them). */
+/* Per-launch timing of wenc_forward, wenc_forward_ctx, wenc_prepare_cross,
+ * wenc_log_mel, wenc_cross_attend and wenc_argmax: HIP events recorded
+ * around every launch whose site bit is set in `site_mask` (bit s =
+ * 1 << WENC_SITE_*), on the stream that launch goes to (the caller's, or
+ * the handle's second stream for the second window group of a forward);
+ * 0 turns it off.  Events are read, and cleared, by wenc_profile_read
+ * (which synchronises on them).  While a mask is set wenc_forward_graph
+ * refuses to record. */
 enum {
     WENC_SITE_INGEST = 0, WENC_SITE_CONV1 = 1, WENC_SITE_CONV2 = 2, WENC_SITE_LN1 = 3,
     WENC_SITE_QKV = 4, WENC_SITE_ATTN = 5, WENC_SITE_OPROJ = 6, WENC_SITE_LN2 = 7,

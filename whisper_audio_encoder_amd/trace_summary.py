@@ -103,15 +103,14 @@ def summarise(path: str, workload: str, parts: int, region: str = "all") -> str:
     per_kernel = defaultdict(list)
     per_site = defaultdict(list)
     intervals = []
-    if True:
-        for row in _rows(path, region):
-            name = row["Kernel_Name"]
-            t0, t1 = int(row["Start_Timestamp"]), int(row["End_Timestamp"])
-            per_kernel[name].append(t1 - t0)
-            s = site_of(name)
-            if s:
-                per_site[s].append((t0, t1))
-            intervals.append((t0, t1, s or "-"))
+    for row in _rows(path, region):
+        name = row["Kernel_Name"]
+        t0, t1 = int(row["Start_Timestamp"]), int(row["End_Timestamp"])
+        per_kernel[name].append(t1 - t0)
+        s = site_of(name)
+        if s:
+            per_site[s].append((t0, t1))
+        intervals.append((t0, t1, s or "-"))
     share, busy = fair_share_ns(intervals)
     total = sum(sum(v) for v in per_kernel.values()) or 1
     forwards = len(per_site.get("lnf", [])) / parts if cfg.final_ln else len(per_site.get("ingest", [])) / parts
