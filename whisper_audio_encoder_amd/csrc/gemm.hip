@@ -429,6 +429,87 @@ gemm_kernel(const GemmP p) {
     static_assert(WN % 64 == 0 && WM % 32 == 0 && (NW / 2) * REGION <= STAGE * 2, "staging fits in one k-step buffer");
     __syncthreads();
     char *stg = reinterpret_cast<char *>(wave < NW / 2 ? smem0 : smem1) + (wave % (NW / 2)) * REGION;
+    // stage the wave's 32-row block i2 of column group cg: lane holds row
+    // 16 g + frow, columns 16 j + 4 hh .. +3 (GELU applied here for conv2)
+    auto stage_f32 = [&](int cg, int i2) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const int cl = j * 16 + 4 * hh;
+                const int srow = 16 * g + frow;
+                const f32x4 v = acc[2 * i2 + g][cg * 4 + j];
+                f32x4 w = v;
+                if constexpr (EPI == WENC_EPI_CONV2) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = gelu_erf(v[e]);
+                }
+                *reinterpret_cast<f32x4 *>(stg + (srow * RS + cl) * 4) = w;
+            }
+    };
+    if constexpr (F32OUT) {
+        // fp32 outputs: out = staged value + addend, where the addend is the
+        // residual (read-modify-write of C) or the position row.  A unit is
+        // a half of a 32-row block: 16 lanes per 64-float row, 4 rows per
+        // instruction, 4 instructions.  Each unit's addend loads are issued
+        // two units ahead, so their latency overlaps the staging, adds and
+        // stores of the units before.  The loads and stores are buffer
+        // operations whose offset is past the range for rows at or beyond M
+        // and columns at or beyond N (a load then reads zero, a store is
+        // dropped), so no branch splits them and the compiler's waits count
+        // exactly the loads a unit needs.  (With a branch per row it waited
+        // for every outstanding load before each store: one full memory
+        // round trip per unit, 8 per 128-row wave tile.)
+        constexpr int UNITS = 2 * (WM / 32);
+        const int c = lane & 15, rq = lane >> 4;
+        // C from the tile's first row on: offsets stay far below 2^31
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<float *>(p.C) + int64_t(m0) * p.ldc, 0, 0x7fffffff, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rpos = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(EPI == WENC_EPI_CONV2 ? p.pos : static_cast<const float *>(p.C)), 0, 0x7fffffff,
+            0x00020000);
+#pragma unroll
+        for (int cg = 0; cg < WN / 64; ++cg) {
+            const int n = n0 + wn * WN + cg * 64 + c * 4;
+            // byte offset in C of row m (tile-relative) and column n, or past the range
+            auto c_off = [&](int m) __attribute__((always_inline)) {
+                return (m < p.M && n < p.N) ? uint32_t(((m - m0) * p.ldc + n) * 4) : OOB;
+            };
+            f32x4 addv[3][4];
+            auto load_unit = [&](int u, f32x4 (&add)[4]) __attribute__((always_inline)) {
+                const int mr = m0 + wm * WM + (u >> 1) * 32;
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int m = mr + ((u & 1) * 4 + it) * 4 + rq;
+                    if constexpr (EPI == WENC_EPI_RESID) {
+                        add[it] = __builtin_amdgcn_raw_buffer_load_b128(rc, c_off(m), 0, 0);
+                    } else {
+                        const uint32_t t = uint32_t(m) - divu(uint32_t(m), p.pos_div) * p.pos_div.d;
+                        const uint32_t off = (m < p.M && n < p.N) ? uint32_t((int(t) * p.N + n) * 4) : OOB;
+                        add[it] = __builtin_amdgcn_raw_buffer_load_b128(rpos, off, 0, 0);
+                    }
+                }
+            };
+            load_unit(0, addv[0]);
+            if (UNITS > 1) load_unit(1, addv[1 % 3]);
+#pragma unroll
+            for (int u = 0; u < UNITS; ++u) {
+                if (u + 2 < UNITS) load_unit(u + 2, addv[(u + 2) % 3]);
+                if ((u & 1) == 0) stage_f32(cg, u >> 1);
+                const int mr = m0 + wm * WM + (u >> 1) * 32;
+                const int h0 = (u & 1) * 4;
+                f32x4 w[4];
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+                    w[it] = *reinterpret_cast<const f32x4 *>(stg + (((h0 + it) * 4 + rq) * RS + c * 4) * 4);
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+                    __builtin_amdgcn_raw_buffer_store_b128(w[it] + addv[u % 3][it], rc, c_off(mr + (h0 + it) * 4 + rq), 0,
+                                                          0);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int cg = 0; cg < WN / 64; ++cg) {
         const int nw = n0 + wn * WN + cg * 64;  // first column of this 64-column group
@@ -453,58 +534,17 @@ gemm_kernel(const GemmP p) {
                     const int cl = j * 16 + 4 * hh;
                     const int srow = 16 * g + frow;
                     const f32x4 v = acc[2 * i2 + g][cg * 4 + j];
-                    if constexpr (F32OUT) {
-                        f32x4 w = v;
-                        if constexpr (EPI == WENC_EPI_CONV2) {
+                    f16x4 o;
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) w[e] = gelu_erf(v[e]);
-                        }
-                        *reinterpret_cast<f32x4 *>(stg + (srow * RS + cl) * 4) = w;
-                    } else {
-                        f16x4 o;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            if constexpr (EPI == WENC_EPI_GELU_F16)
-                                o[e] = (f16)gelu_erf(v[e]);
-                            else
-                                o[e] = (f16)(v[e] * sc);
-                        }
-                        *reinterpret_cast<f16x4 *>(stg + (srow * RS + cl) * 2) = o;
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (EPI == WENC_EPI_GELU_F16)
+                            o[e] = (f16)gelu_erf(v[e]);
+                        else
+                            o[e] = (f16)(v[e] * sc);
                     }
+                    *reinterpret_cast<f16x4 *>(stg + (srow * RS + cl) * 2) = o;
                 }
-            if constexpr (F32OUT) {
-                // 16 lanes per 64-float row, 4 rows per instruction, in two
-                // halves of 4 instructions whose residual (or position) reads
-                // are all issued before their adds
-                const int c = lane & 15, rq = lane >> 4;
-                const int n = nw + c * 4;
-#pragma unroll
-                for (int h0 = 0; h0 < 8; h0 += 4) {
-                    f32x4 w[4], add[4];
-#pragma unroll
-                    for (int it = 0; it < 4; ++it)
-                        w[it] = *reinterpret_cast<const f32x4 *>(stg + (((h0 + it) * 4 + rq) * RS + c * 4) * 4);
-#pragma unroll
-                    for (int it = 0; it < 4; ++it) {
-                        const int m = mr + (h0 + it) * 4 + rq;
-                        add[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        if (m < p.M && n < p.N) {
-                            if constexpr (EPI == WENC_EPI_RESID) {
-                                add[it] = ld4(static_cast<const float *>(p.C) + int64_t(m) * p.ldc + n);
-                            } else {
-                                const uint32_t t = m - divu(m, p.pos_div) * p.pos_div.d;
-                                add[it] = ld4(p.pos + int64_t(t) * p.N + n);
-                            }
-                        }
-                    }
-#pragma unroll
-                    for (int it = 0; it < 4; ++it) {
-                        const int m = mr + (h0 + it) * 4 + rq;
-                        if (m < p.M && n < p.N)
-                            *reinterpret_cast<f32x4 *>(static_cast<float *>(p.C) + int64_t(m) * p.ldc + n) = w[it] + add[it];
-                    }
-                }
-            } else if (vtile) {
+            if (vtile) {
                 if constexpr (EPI == WENC_EPI_QKV) {
                     // V^T [b][h][dim][slot]: the block's 32 rows are two 16-key
                     // groups of one batch item each (the row space is padded to a
@@ -659,10 +699,13 @@ const char *gemm_check(const wenc_gemm_args &a) {
             if (!a.C || !a.pos) return "gemm: C and pos must be non-null";
             if (a.pos_rows <= 0 || a.pos_rows >= (1 << 16)) return "gemm: pos_rows out of range";
             if (a.ldc < a.N) return "gemm: ldc < N";
+            if (int64_t(a.pos_rows) * a.N * 4 >= (int64_t(1) << 31)) return "gemm: position table too large for 31-bit offsets";
+            if (int64_t(a.ldc) * 256 * 4 >= (int64_t(1) << 30)) return "gemm: C rows too long for 31-bit tile offsets";
             break;
         case WENC_EPI_RESID:
             if (!a.C) return "gemm: C is null";
             if (a.ldc < a.N) return "gemm: ldc < N";
+            if (int64_t(a.ldc) * 256 * 4 >= (int64_t(1) << 30)) return "gemm: C rows too long for 31-bit tile offsets";
             break;
         case WENC_EPI_QKV:
             if (!a.q || !a.k || !a.vt) return "gemm: q, k, vt must be non-null";

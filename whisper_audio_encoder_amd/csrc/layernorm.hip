@@ -46,19 +46,37 @@ ln_kernel(const float *__restrict__ x, const float *__restrict__ g, const float 
           void *__restrict__ y, int rows, int d, float eps) {
     const int lane = threadIdx.x & 63;
     const int nwaves = gridDim.x * 4;
-    int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    // (readfirstlane: the row is uniform across the wave, so the buffer
+    // descriptors below stay in scalar registers)
+    int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
     const int nv = d >> 2;
-    const float4 *g4 = reinterpret_cast<const float4 *>(g);
-    const float4 *b4 = reinterpret_cast<const float4 *>(bta);
-    float4 v[NV], vn[NV];
+    float4 v[NV], vn[NV], gg[NV], bb[NV];
+    // Buffer loads over the one row (a row past the last one has an empty
+    // range): columns past d read zero without a branch, so the compiler's
+    // wait before the current row's use counts the next row's loads exactly
+    // instead of waiting for them too.
     auto load = [&](int r, float4 (&dst)[NV]) {
-        const float4 *xr = reinterpret_cast<const float4 *>(x + int64_t(r) * d);
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(x) + int64_t(r < rows ? r : 0) * d, 0, r < rows ? d * 4 : 0, 0x00020000);
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            const int i = lane + 64 * j;
-            dst[j] = (r < rows && i < nv) ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const f32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rx, uint32_t(lane + 64 * j) * 16u, 0, 0);
+            dst[j] = make_float4(t[0], t[1], t[2], t[3]);
         }
     };
+    // the gains and biases once per wave, before the rows (no load inside
+    // the row loop but the next row's)
+    {
+        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(g), 0, d * 4, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(bta), 0, d * 4, 0x00020000);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const f32x4 tg = __builtin_amdgcn_raw_buffer_load_b128(rg, uint32_t(lane + 64 * j) * 16u, 0, 0);
+            const f32x4 tb = __builtin_amdgcn_raw_buffer_load_b128(rb, uint32_t(lane + 64 * j) * 16u, 0, 0);
+            gg[j] = make_float4(tg[0], tg[1], tg[2], tg[3]);
+            bb[j] = make_float4(tb[0], tb[1], tb[2], tb[3]);
+        }
+    }
     load(row, v);
     for (; row < rows; row += nwaves) {
         load(row + nwaves, vn);
@@ -80,11 +98,10 @@ ln_kernel(const float *__restrict__ x, const float *__restrict__ g, const float 
         for (int j = 0; j < NV; ++j) {
             const int i = lane + 64 * j;
             if (i < nv) {
-                const float4 gg = g4[i], bb = b4[i];
-                const float o0 = (v[j].x - mean) * rstd * gg.x + bb.x;
-                const float o1 = (v[j].y - mean) * rstd * gg.y + bb.y;
-                const float o2 = (v[j].z - mean) * rstd * gg.z + bb.z;
-                const float o3 = (v[j].w - mean) * rstd * gg.w + bb.w;
+                const float o0 = (v[j].x - mean) * rstd * gg[j].x + bb[j].x;
+                const float o1 = (v[j].y - mean) * rstd * gg[j].y + bb[j].y;
+                const float o2 = (v[j].z - mean) * rstd * gg[j].z + bb[j].z;
+                const float o3 = (v[j].w - mean) * rstd * gg[j].w + bb[j].w;
                 if constexpr (OUT32) {
                     reinterpret_cast<float4 *>(static_cast<float *>(y) + int64_t(row) * d)[i] = make_float4(o0, o1, o2, o3);
                 } else {
