@@ -166,7 +166,8 @@ const char *wenc_last_error(const wenc_t *h);
  * periodic Hann window and reflect padding (frames centred, the last STFT
  * frame dropped); n_mels area-normalised triangles on the Slaney mel scale
  * over 0 .. 8 kHz; log10 of max(power, 1e-10); clamp at the window's maximum
- * minus 8 (-80 dB); (x + 4) / 4.  All in fp32.
+ * minus 8 (-80 dB); (x + 4) / 4.  All in fp32; the STFT is the 20 x 20
+ * mixed-radix FFT of the same section.
  *   audio: device fp32 [batch][160 * n_frames], 16 kHz mono, already padded
  *          or cut to the window (480,000 samples for 3000 frames); 4-byte
  *          aligned;

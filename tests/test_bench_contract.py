@@ -33,7 +33,7 @@ def test_site_work_covers_every_profiled_site(name):
     work = bench.site_work(cfg, cfg.batch)
     assert set(wenc.SITES) <= set(work)
     for site, (kind, amount) in work.items():
-        assert kind in ("mfma", "hbm") and amount > 0, site
+        assert kind in ("mfma", "hbm", "alu") and amount > 0, site
     # the MFMA sites add up to the metric's FLOPs per window times the batch
     per_batch = sum(work[s][1] for s in ("conv1", "conv2")) + cfg.n_layer * sum(
         work[s][1] for s in ("qkv", "attn", "oproj", "fc1", "fc2"))

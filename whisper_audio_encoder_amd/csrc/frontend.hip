@@ -10,15 +10,28 @@
 // the STFT's last frame is dropped, so a window of 160 F samples gives F
 // frames; power is floored at 1e-10 before the logarithm.
 //
-// The STFT is a dense contraction per frame (X[t][k] = sum_n w[n] x[160 t -
-// 200 + n] e^{-2 pi i k n / 400}), computed as fp32 MFMA (32x32x2) products:
-// the frequency-by-sample basis (cos, -sin from a 400-entry table indexed by
-// k n mod 400) is the A operand, the windowed samples the B operand.  The
-// power tile that comes out is, register for register, already the B
-// operand of the mel projection (summing k in the order the accumulator
-// holds it), so power never leaves registers.  fp32 throughout: the -80 dB
-// clamp keeps bins down to 1e-8 of the peak power, below what fp16 operands
-// resolve.
+// The STFT of a frame, X[k] = sum_j w[j] x[160 t - 200 + j] W^{jk} with
+// W = e^{-2 pi i / 400}, is the 20 x 20 mixed-radix FFT the same section
+// names.  With j = 20 a + c and k = p + 20 q (a, c, p in [0, 20)):
+//   Y[p][c] = sum_a xw[20 a + c] W20^{a p}          (20-point DFTs of real data)
+//   Z[p][c] = Y[p][c] W^{c p}                       (twiddles)
+//   X[p + 20 q] = sum_c Z[p][c] W20^{c q}            (20-point DFTs over c)
+// where W20 = W^20.  The data are real, so Y[20 - p] = conj(Y[p]) and only
+// p <= 10 is formed; the second stage forms q = 0 .. 10 and keeps k <= 200.
+// Both 20-point DFTs pair opposite inputs (j and 20 - j) so each output needs
+// 9 products per part; cos and sin of 2 pi m / 20 are compile-time constants
+// and products by 0 and +-1 are not issued.  fp32 throughout: the -80 dB clamp
+// keeps bins down to 1e-8 of the peak power, below what fp16 resolves.
+//
+// The mel projection reads each triangle through a window of 16 n_ch bins
+// that holds all of its non-zero weights (16 for the 80- and 128-filter
+// banks, against 201 for a dense row), summed in increasing bin order.
+//
+// A 320-thread workgroup takes 16 frames of one window at a time: the
+// samples, window, twiddles, the Z grid and the power rows live in LDS;
+// thread (f, c) runs the first stage of frame f for column c, thread (f, p)
+// the second stage for row p, and thread (g, m) sums filter m over every
+// G-th frame from g, its weights in registers.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,19 +40,40 @@ namespace {
 
 constexpr int NFFT = 400;
 constexpr int HOP = 160;
-constexpr int NBIN = NFFT / 2 + 1;  // 201
-constexpr int KT = 7;               // frequency tiles of 32
-constexpr int KPAD = KT * 32;
-static_assert(KPAD >= NBIN, "the frequency tiles cover every bin");
-constexpr int TF = 32;              // frames per workgroup (one wave)
-constexpr int SPAN = HOP * (TF - 1) + NFFT;  // samples the 32 frames read: 5360
-constexpr int NSEG = (SPAN + HOP - 1) / HOP;  // 160-sample segments: 34
-// Staged sample p sits at p + p / 160: each hop segment is followed by one
-// pad float, so frame t starts at 161 t, whose LDS bank (161 t mod 64 =
-// 33 t mod 64) differs for all 32 frames a B-operand read touches.
-constexpr int XS = NSEG * (HOP + 1);
+constexpr int R = 20;                        // 400 = 20 x 20
+constexpr int TF = 16;                       // frames per workgroup
+constexpr int NT = TF * R;                   // 320 threads
+constexpr int SPAN = HOP * (TF - 1) + NFFT;  // samples the 16 frames read: 2800
+constexpr int ZS = R + 1;                    // float2 stride of a Z row: conflict-free row reads
+constexpr int PS = 204;                      // power row stride (201 bins)
+constexpr int XSZ = SPAN > TF * PS ? SPAN : TF * PS;  // samples, then (stage 2 on) power rows
+constexpr int NLD = (SPAN + NT - 1) / NT;    // samples staged per thread
+constexpr int NXW = (LOGMEL_MAX_EXTRA + NT - 1) / NT;  // extra mel weights staged per thread
+constexpr int KF = 8;                        // frames per mel thread: at most 16 / G, G = 320 / n_mels >= 2
+static_assert(2 * NT >= NFFT && NT >= 2 * LOGMEL_MAX_MELS, "one pass stages the tables; G >= 2");
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// cos and sin of 2 pi m / 20 (cos 18 deg, cos 36 deg, cos 54 deg, cos 72 deg).
+constexpr float C1 = 0.951056516295153572f;
+constexpr float C2 = 0.809016994374947424f;
+constexpr float C3 = 0.587785252292473129f;
+constexpr float C4 = 0.309016994374947424f;
+__device__ constexpr float cos20(int m) {
+    constexpr float t[R] = {1.f, C1, C2, C3, C4, 0.f, -C4, -C3, -C2, -C1, -1.f, -C1, -C2, -C3, -C4, 0.f, C4, C3, C2, C1};
+    return t[m % R];
+}
+__device__ constexpr float sin20(int m) { return cos20(m + 15); }  // sin x = cos(x - pi / 2)
+
+// acc + x k for a constant k known once the loops are unrolled: nothing for
+// 0, an add or a subtract for +-1 (exact, as the fused form would be).
+__device__ __forceinline__ float mac(float acc, float x, float k) {
+    if (k == 0.0f) return acc;
+    if (k == 1.0f) return acc + x;
+    if (k == -1.0f) return acc - x;
+    return __builtin_fmaf(x, k, acc);
+}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -47,115 +81,205 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// One workgroup = one wave = frames t0 .. t0+31 of window b.
-__global__ void __launch_bounds__(64)
-logmel_kernel(const float *__restrict__ audio, int n_samples, int n_frames, const f32x2 *__restrict__ tab,
-              const float *__restrict__ win, const float *__restrict__ filt, int n_mels, int mtiles,
-              float *__restrict__ out, float *__restrict__ blkmax) {
-    __shared__ float xs[XS];
-    __shared__ f32x2 tb[NFFT];
+// Persistent: workgroup w takes jobs w, w + grid, ...; job j is frames
+// 16 tile .. 16 tile + 15 of window b = j / tiles, tile = j % tiles.  The
+// next job's samples are loaded into registers while the current one is
+// computed.
+__global__ void __launch_bounds__(NT)
+logmel_kernel(const float *__restrict__ audio, int n_samples, int n_frames, int tiles, int jobs,
+              const f32x2 *__restrict__ tab, const float *__restrict__ win, const float *__restrict__ mwt,
+              const int *__restrict__ mstart, int nch, int n_mels, float *__restrict__ out,
+              float *__restrict__ blkmax) {
+    __shared__ float xs[XSZ];          // samples of the job; power rows from the second stage on
+    __shared__ f32x2 zs[TF * R * ZS];  // Z[f][p][c]
+    __shared__ f32x2 tw[NFFT];         // W^m = (cos, -sin) of 2 pi m / 400
     __shared__ float wn[NFFT];
-    const int b = blockIdx.y, tile = blockIdx.x, t0 = tile * TF, lane = threadIdx.x;
-    const float *x = audio + int64_t(b) * n_samples;
+    __shared__ float wx[LOGMEL_MAX_EXTRA];  // mel windows 1 .. nch - 1 of every filter
+    __shared__ float wmax[NT / 64];
+    const int tid = threadIdx.x;
+    const int64_t limit_off = int64_t(HOP) * (n_frames - 1) + NFFT / 2;  // samples past this are read by no frame
 
-    // Stage the samples, reflected about the first and last sample (the edge
-    // sample itself is not repeated).  Samples no valid frame reads are 0.
-    const int64_t s0 = int64_t(HOP) * t0 - NFFT / 2;
-    const int64_t limit = int64_t(HOP) * (n_frames - 1) + NFFT / 2;
-    for (int p = lane; p < SPAN; p += 64) {
-        const int64_t s = s0 + p;
-        float v = 0.0f;
-        if (s < limit) {
-            const int64_t i = s < 0 ? -s : (s >= n_samples ? 2 * int64_t(n_samples - 1) - s : s);
-            v = x[i];
-        }
-        xs[p + p / HOP] = v;
-    }
-    for (int i = lane; i < NFFT; i += 64) {
-        tb[i] = tab[i];
-        wn[i] = win[i];
-    }
-    __syncthreads();
-
-    // A operand (basis): lane l supplies frequency k = 32 kt + (l & 31) at
-    // sample n = 2 s + (l >> 5).  B operand (samples): lane l supplies frame
-    // t = l & 31 at the same n.  Accumulator register r of lane l then holds
-    // frame l & 31 and frequency 32 kt + 8 (r >> 2) + 4 (l >> 5) + (r & 3).
-    const int t = lane & 31, hh = lane >> 5;
-    const float *xb = xs + (HOP + 1) * t + hh;
-    const float *wb = wn + hh;
-    f32x16 mel[4];
+    // Reflected sample loads of job j into registers (the edge sample itself
+    // is not repeated; samples no valid frame reads are 0).
+    float xv[NLD];
+    auto load_job = [&](int j) {
+        const int bj = j / tiles, t0 = (j - bj * tiles) * TF;
+        const float *x = audio + int64_t(bj) * n_samples;
+        const int64_t s0 = int64_t(HOP) * t0 - NFFT / 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mel[i][r] = 0.0f;
-
-#pragma unroll 1
-    for (int kt = 0; kt < KT; ++kt) {
-        const uint32_t k = uint32_t(kt * 32 + t);
-        const uint32_t dk = (2 * k) % NFFT;
-        uint32_t idx = (k * uint32_t(hh)) % NFFT;
-        f32x16 re, im;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) re[r] = im[r] = 0.0f;
-        auto step = [&](int s, int seg) {
-            const float bx = xb[2 * s + seg] * wb[2 * s];
-            const f32x2 a = tb[idx];
-            re = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, bx, re, 0, 0, 0);
-            im = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, bx, im, 0, 0, 0);
-            idx += dk;
-            idx = min(idx, idx - uint32_t(NFFT));  // idx - 400 wraps above 2^31 while idx < 400
-        };
-        // n = 2 s + (l >> 5) crosses a hop segment (one pad float) at s = 80 and 160
-#pragma unroll 8
-        for (int s = 0; s < 80; ++s) step(s, 0);
-#pragma unroll 8
-        for (int s = 80; s < 160; ++s) step(s, 1);
-#pragma unroll 8
-        for (int s = 160; s < 200; ++s) step(s, 2);
-
-        f32x16 pw;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pw[r] = re[r] * re[r] + im[r] * im[r];
-        // Mel projection: A' = filters (lane l: filter 32 mt + (l & 31)), B' =
-        // power; MFMA step r sums frequency 32 kt + 8 (r >> 2) + 4 h + (r & 3)
-        // for lane half h, exactly the frequency pw[r] holds.
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            if (mt >= mtiles) break;
-            const float *fr = filt + (mt * 32 + t) * KPAD + kt * 32 + 4 * hh;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 f = *reinterpret_cast<const f32x4 *>(fr + 8 * g);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    mel[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(f[e], pw[4 * g + e], mel[mt], 0, 0, 0);
+        for (int u = 0; u < NLD; ++u) {
+            const int p = tid + u * NT;
+            const int64_t s = s0 + p;
+            xv[u] = 0.0f;
+            if (p < SPAN && s < limit_off) {
+                const int64_t i = s < 0 ? -s : (s >= n_samples ? 2 * int64_t(n_samples - 1) - s : s);
+                xv[u] = x[i];
             }
         }
-    }
+    };
 
-    // log10(max(m, 1e-10)) in the mel accumulators' layout: lane l holds
-    // frame t0 + (l & 31) and filters 32 mt + 8 g + 4 h + e, stored as runs of 4.
-    const int frame = t0 + t;
-    float mx = -3.0e38f;
+    // Mel work: thread (g, m), m = tid % n_mels, g = tid / n_mels < G, sums
+    // filter m for frames g, g + G, ...  Its first 16 weights stay in
+    // registers (the whole triangle for 72 or more filters).
+    const int G = min(TF, NT / n_mels);
+    const int g = tid / n_mels, m = tid - g * n_mels;
+    const bool mel_lane = g < G;
+    float w0[16];
+    int ms = 0;
+    if (mel_lane) {
+        ms = mstart[m];
+        const f32x4 *wp = reinterpret_cast<const f32x4 *>(mwt + int64_t(m) * nch * 16);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        if (mt >= mtiles) break;
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 v = wp[q];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int m = mt * 32 + 8 * g + 4 * hh;
-            f32x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[e] = __builtin_amdgcn_logf(fmaxf(mel[mt][4 * g + e], 1e-10f)) * 0.30102999566398120f;
-            if (frame < n_frames && m < n_mels) {
-                *reinterpret_cast<f32x4 *>(out + (int64_t(b) * n_frames + frame) * n_mels + m) = v;
-                mx = fmaxf(mx, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-            }
+            for (int e = 0; e < 4; ++e) w0[4 * q + e] = v[e];
         }
     }
-    mx = wave_max(mx);
-    if (lane == 0) blkmax[int64_t(b) * gridDim.x + tile] = mx;
+    // the tables (every global load here is issued before the first LDS store)
+    f32x2 tv[2];
+    float wv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + u * NT;
+        if (i < NFFT) {
+            tv[u] = tab[i];
+            wv[u] = win[i];
+        }
+    }
+    const int nx = n_mels * (nch - 1) * 16;  // <= LOGMEL_MAX_EXTRA
+    float xw[NXW];
+#pragma unroll
+    for (int u = 0; u < NXW; ++u) {
+        const int i = tid + u * NT;
+        xw[u] = 0.0f;
+        if (i < nx) xw[u] = mwt[(i >> 4) / (nch - 1) * nch * 16 + 16 + (i >> 4) % (nch - 1) * 16 + (i & 15)];
+    }
+    int job = blockIdx.x;
+    if (job < jobs) load_job(job);
+#pragma unroll
+    for (int u = 0; u < NXW; ++u)
+        if (tid + u * NT < nx) wx[tid + u * NT] = xw[u];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + u * NT;
+        if (i < NFFT) {
+            tw[i] = tv[u];
+            wn[i] = wv[u];
+        }
+    }
+
+    for (; job < jobs; job += gridDim.x) {
+        const int b = job / tiles, tile = job - b * tiles, t0 = tile * TF;
+#pragma unroll
+        for (int u = 0; u < NLD; ++u)
+            if (tid + u * NT < SPAN) xs[tid + u * NT] = xv[u];
+        __syncthreads();
+        if (job + int(gridDim.x) < jobs) load_job(job + gridDim.x);
+
+        // First stage: thread (f, c), f = tid / 20.  Frame f's sample j sits
+        // at xs[160 f + j].
+        {
+            const int f = tid / R, c = tid - f * R;
+            const float *xf = xs + HOP * f + c;
+            float xa[R];
+#pragma unroll
+            for (int a = 0; a < R; ++a) xa[a] = xf[R * a] * wn[R * a + c];
+            float u[10], v[10];
+#pragma unroll
+            for (int a = 1; a < 10; ++a) {
+                u[a] = xa[a] + xa[R - a];
+                v[a] = xa[a] - xa[R - a];
+            }
+            float yr[11], yi[11];
+#pragma unroll
+            for (int p = 0; p <= 10; ++p) {
+                float re = (p & 1) ? xa[0] - xa[10] : xa[0] + xa[10];
+                float im = 0.0f;
+#pragma unroll
+                for (int a = 1; a < 10; ++a) {
+                    re = mac(re, u[a], cos20(a * p));
+                    im = mac(im, v[a], -sin20(a * p));
+                }
+                yr[p] = re;
+                yi[p] = im;
+            }
+            f32x2 *zc = zs + f * R * ZS + c;
+            zc[0] = f32x2{yr[0], yi[0]};
+#pragma unroll
+            for (int p = 1; p < R; ++p) {
+                const float y_r = p <= 10 ? yr[p] : yr[R - p];
+                const float y_i = p <= 10 ? yi[p] : -yi[R - p];
+                const f32x2 w = tw[c * p];  // c p <= 361
+                zc[p * ZS] = f32x2{y_r * w.x - y_i * w.y, __builtin_fmaf(y_r, w.y, y_i * w.x)};
+            }
+        }
+        __syncthreads();
+
+        // Second stage: thread (f, p) reads row p of frame f's Z (row index
+        // f 20 + p = tid) and writes bins p + 20 q; q = 10 only exists for p = 0.
+        {
+            const int f = tid / R, p = tid - f * R;
+            const f32x2 *zr = zs + tid * ZS;
+            f32x2 z[R];
+#pragma unroll
+            for (int c = 0; c < R; ++c) z[c] = zr[c];
+            f32x2 sm[10], df[10];
+#pragma unroll
+            for (int c = 1; c < 10; ++c) {
+                sm[c] = z[c] + z[R - c];
+                df[c] = z[c] - z[R - c];
+            }
+            float *pw = xs + f * PS;
+#pragma unroll
+            for (int q = 0; q <= 10; ++q) {
+                float re = (q & 1) ? z[0].x - z[10].x : z[0].x + z[10].x;
+                float im = (q & 1) ? z[0].y - z[10].y : z[0].y + z[10].y;
+#pragma unroll
+                for (int c = 1; c < 10; ++c) {
+                    const float cs = cos20(c * q), sn = sin20(c * q);
+                    re = mac(mac(re, sm[c].x, cs), df[c].y, sn);
+                    im = mac(mac(im, sm[c].y, cs), df[c].x, -sn);
+                }
+                if (q < 10 || p == 0) pw[p + R * q] = __builtin_fmaf(re, re, im * im);
+            }
+        }
+        __syncthreads();
+
+        // Mel sums over bins ms .. ms + 16 nch - 1 in increasing order (the
+        // weights are zero outside the triangle), then log10(max(m, 1e-10)).
+        float mx = -3.0e38f;
+        const int nvalid = min(TF, n_frames - t0);
+        if (mel_lane) {
+            float *o = out + (int64_t(b) * n_frames + t0) * n_mels + m;
+#pragma unroll 2
+            for (int k = 0; k < KF; ++k) {
+                const int f = g + G * k;
+                if (f >= nvalid) break;
+                const float *pr = xs + f * PS + ms;
+                float acc = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) acc = __builtin_fmaf(pr[j], w0[j], acc);
+                for (int ch = 1; ch < nch; ++ch) {  // narrow filter banks only: later windows from LDS
+                    const float *w = wx + (m * (nch - 1) + ch - 1) * 16;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) acc = __builtin_fmaf(pr[16 * ch + j], w[j], acc);
+                }
+                const float v = __builtin_amdgcn_logf(fmaxf(acc, 1e-10f)) * 0.30102999566398120f;
+                o[int64_t(f) * n_mels] = v;
+                mx = fmaxf(mx, v);
+            }
+        }
+        mx = wave_max(mx);
+        if ((tid & 63) == 0) wmax[tid >> 6] = mx;
+        __syncthreads();
+        if (tid == 0) {
+            float mm = wmax[0];
+#pragma unroll
+            for (int w = 1; w < NT / 64; ++w) mm = fmaxf(mm, wmax[w]);
+            blkmax[int64_t(b) * tiles + tile] = mm;
+        }
+    }
 }
 
 // x = (max(x, M - 8) + 4) / 4 over window b, M the window's maximum.
@@ -186,17 +310,20 @@ const char *logmel_check(int batch, int n_frames, int n_mels) {
     if (batch < 0 || batch > 65535) return "log_mel: batch outside [0, 65535]";
     if (n_frames < 2) return "log_mel: n_frames must be >= 2 (the reflect padding needs more than 200 samples)";
     if (int64_t(n_frames) * HOP >= (int64_t(1) << 31)) return "log_mel: window too long";
-    if (n_mels <= 0 || n_mels > 128 || n_mels % 8) return "log_mel: n_mels must be a multiple of 8, <= 128";
+    if (n_mels <= 0 || n_mels > LOGMEL_MAX_MELS || n_mels % 8) return "log_mel: n_mels must be a multiple of 8, <= 128";
     return nullptr;
 }
 
 hipError_t launch_logmel(const float *audio, int batch, int n_frames, const float *tab, const float *win,
-                         const float *filt, int n_mels, float *out, float *blkmax, hipStream_t s) {
+                         const float *mwt, const int *mstart, int nch, int n_mels, float *out, float *blkmax,
+                         hipStream_t s) {
     if (batch == 0) return hipSuccess;
-    const int tiles = logmel_tiles(n_frames);
-    logmel_kernel<<<dim3(tiles, batch), dim3(64), 0, s>>>(audio, n_frames * HOP, n_frames,
-                                                          reinterpret_cast<const f32x2 *>(tab), win, filt, n_mels,
-                                                          (n_mels + 31) / 32, out, blkmax);
+    if (nch < 1 || 16 * nch > 201 || n_mels * (nch - 1) * 16 > LOGMEL_MAX_EXTRA) return hipErrorInvalidValue;
+    const int tiles = logmel_tiles(n_frames), jobs = tiles * batch;
+    const int grid = int(std::min<long>(jobs, 2 * cu_count()));  // two workgroups fit a compute unit's LDS
+    logmel_kernel<<<dim3(grid), dim3(NT), 0, s>>>(audio, n_frames * HOP, n_frames, tiles, jobs,
+                                                  reinterpret_cast<const f32x2 *>(tab), win, mwt, mstart, nch,
+                                                  n_mels, out, blkmax);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n4 = int64_t(n_frames) * n_mels / 4;

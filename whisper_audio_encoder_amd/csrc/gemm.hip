@@ -647,6 +647,8 @@ TileMode &tile_mode() {
     return m;
 }
 
+}  // namespace
+
 // Compute units of the current device (cached per device; a race only
 // stores the same value twice).
 long cu_count() {
@@ -660,8 +662,6 @@ long cu_count() {
     }
     return n;
 }
-
-}  // namespace
 
 int gemm_mode(int tile, int split) {
     if (tile < -1 || tile > 1 || split < 0 || split > 1) return -1;

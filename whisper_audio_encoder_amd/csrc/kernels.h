@@ -42,12 +42,19 @@ hipError_t launch_ingest(const float *mel, uint16_t *melp, uint16_t *c1, int B, 
 
 // Log-mel frontend: audio fp32 [batch][160 n_frames] -> out fp32
 // [batch][n_frames][n_mels].  tab: [400] (cos, -sin) pairs of 2 pi i / 400;
-// win: [400] periodic Hann; filt: [32 ceil(n_mels / 32)][224] fp32 Slaney
-// filters, zero beyond bin 200 and filter n_mels - 1; blkmax: [batch][tiles].
+// win: [400] periodic Hann; filter m's weights at bins mstart[m] .. mstart[m]
+// + 16 nch - 1 are mwt[m][0 .. 16 nch) (16-byte aligned rows, zero outside
+// the triangle, mstart[m] + 16 nch <= 201); blkmax: [batch][tiles].
+constexpr int LOGMEL_MAX_MELS = 128;
+constexpr int LOGMEL_MAX_EXTRA = 1024;  // n_mels (nch - 1) 16: the weights past each filter's first 16 bins
 int logmel_tiles(int n_frames);
 const char *logmel_check(int batch, int n_frames, int n_mels);
 hipError_t launch_logmel(const float *audio, int batch, int n_frames, const float *tab, const float *win,
-                         const float *filt, int n_mels, float *out, float *blkmax, hipStream_t s);
+                         const float *mwt, const int *mstart, int nch, int n_mels, float *out, float *blkmax,
+                         hipStream_t s);
+
+// Compute units of the current device (cached per device).
+long cu_count();
 
 // Decode-step cross-attention (xattn.hip): q fp16 [batch][n_q][64 n_head],
 // xk, xv fp16 [batch][T][64 n_head] (16-byte aligned), out fp16 like q;

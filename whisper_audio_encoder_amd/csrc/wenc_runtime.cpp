@@ -169,10 +169,14 @@ double mel_to_hz_slaney(double m) { return m < 15.0 ? m * (200.0 / 3.0) : 1000.0
 // rounded to fp32: (cos, -sin) of 2 pi i / 400; the periodic Hann window
 // 0.5 - 0.5 cos(2 pi i / 400); and n_mels triangles whose corners are
 // evenly spaced in Slaney mels from 0 Hz to 8 kHz, each scaled by 2 / (its
-// width in Hz) (unit area), sampled at the 201 bins k * 40 Hz and stored
-// [32 ceil(n_mels / 32)][224] with zero padding.
+// width in Hz) (unit area), sampled at the 201 bins k * 40 Hz.  Filter m is
+// kept as a window of 16 nch bins from mstart[m] that holds every non-zero
+// weight (nch the same for all filters, the window inside bins 0 .. 200):
+// mwt[m][i] is the weight of bin mstart[m] + i, zero outside the triangle.
 struct FrontendTables {
-    std::vector<float> tab, win, filt;
+    std::vector<float> tab, win, mwt;
+    std::vector<int32_t> mstart;
+    int nch = 1;
 };
 
 FrontendTables frontend_tables(int n_mels) {
@@ -186,19 +190,34 @@ FrontendTables frontend_tables(int n_mels) {
         t.tab[2 * i + 1] = float(-std::sin(a));
         t.win[i] = float(0.5 - 0.5 * std::cos(a));
     }
-    const int rows = (n_mels + 31) / 32 * 32;
-    t.filt.assign(size_t(rows) * 224, 0.0f);
     const double top = hz_to_mel_slaney(8000.0);
     std::vector<double> c(n_mels + 2);
     for (int i = 0; i < n_mels + 2; ++i) c[i] = mel_to_hz_slaney(top * i / (n_mels + 1));
+    std::vector<float> dense(size_t(n_mels) * 201);
+    std::vector<int> first(n_mels, -1), last(n_mels, -1);
     for (int i = 0; i < n_mels; ++i)
         for (int k = 0; k <= 200; ++k) {
             const double hz = 40.0 * k;
             const double rise = (hz - c[i]) / (c[i + 1] - c[i]);
             const double fall = (c[i + 2] - hz) / (c[i + 2] - c[i + 1]);
-            const double w = std::max(0.0, std::min(rise, fall)) * 2.0 / (c[i + 2] - c[i]);
-            t.filt[size_t(i) * 224 + k] = float(w);
+            const float w = float(std::max(0.0, std::min(rise, fall)) * 2.0 / (c[i + 2] - c[i]));
+            dense[size_t(i) * 201 + k] = w;
+            if (w != 0.0f) {
+                if (first[i] < 0) first[i] = k;
+                last[i] = k;
+            }
         }
+    for (int i = 0; i < n_mels; ++i)
+        if (first[i] >= 0) t.nch = std::max(t.nch, (last[i] - first[i] + 16) / 16);
+    const int width = 16 * t.nch;
+    t.mstart.assign(n_mels, 0);
+    t.mwt.assign(size_t(n_mels) * width, 0.0f);
+    for (int i = 0; i < n_mels; ++i) {
+        if (first[i] < 0) continue;  // an empty triangle: all weights zero
+        const int s = std::max(0, std::min(first[i], 201 - width));
+        t.mstart[i] = s;
+        for (int k = first[i]; k <= last[i]; ++k) t.mwt[size_t(i) * width + (k - s)] = dense[size_t(i) * 201 + k];
+    }
     return t;
 }
 
@@ -220,7 +239,8 @@ struct wenc {
     char *sarena = nullptr;
     char *xarena = nullptr;  // cross-attention K/V weights (wenc_load_cross)
     char *farena = nullptr;  // log-mel tables and per-tile maxima (when n_mels suits the frontend)
-    size_t f_win = 0, f_filt = 0, f_blk = 0;
+    size_t f_win = 0, f_mwt = 0, f_mstart = 0, f_blk = 0;
+    int f_nch = 1;  // 16-bin windows per mel filter in the log-mel tables
     int n_dec = 0;
     size_t x_stride = 0;     // bytes per decoder layer in xarena: W_kv fp16 [2d][d], then bias fp32 [2d]
     WeightLayout wl;
@@ -599,14 +619,21 @@ int wenc_create(const wenc_config *cfg, wenc_t **out) {
         Bump fb;
         const size_t tab = fb.take(4 * t.tab.size());
         h->f_win = fb.take(4 * t.win.size());
-        h->f_filt = fb.take(4 * t.filt.size());
+        h->f_mwt = fb.take(4 * t.mwt.size());
+        h->f_mstart = fb.take(4 * t.mstart.size());
+        h->f_nch = t.nch;
         h->f_blk = fb.take(4 * size_t(cfg->max_batch) * wk::logmel_tiles(cfg->n_frames));
-        rc = alloc(&h->farena, fb.off, "log-mel tables");
-        if (rc == WENC_OK) {
+        // every filter's window lies within the 201 bins (otherwise the handle
+        // has no frontend and wenc_log_mel reports it)
+        bool ok = 16 * t.nch <= 201 && cfg->n_mels * (t.nch - 1) * 16 <= wk::LOGMEL_MAX_EXTRA;
+        for (int i = 0; ok && i < cfg->n_mels; ++i) ok = t.mstart[i] >= 0 && t.mstart[i] + 16 * t.nch <= 201;
+        if (ok) rc = alloc(&h->farena, fb.off, "log-mel tables");
+        if (ok && rc == WENC_OK) {
             e = hipMemcpy(h->farena + tab, t.tab.data(), 4 * t.tab.size(), hipMemcpyHostToDevice);
             if (e == hipSuccess) e = hipMemcpy(h->farena + h->f_win, t.win.data(), 4 * t.win.size(), hipMemcpyHostToDevice);
+            if (e == hipSuccess) e = hipMemcpy(h->farena + h->f_mwt, t.mwt.data(), 4 * t.mwt.size(), hipMemcpyHostToDevice);
             if (e == hipSuccess)
-                e = hipMemcpy(h->farena + h->f_filt, t.filt.data(), 4 * t.filt.size(), hipMemcpyHostToDevice);
+                e = hipMemcpy(h->farena + h->f_mstart, t.mstart.data(), 4 * t.mstart.size(), hipMemcpyHostToDevice);
             if (e != hipSuccess) rc = fail(nullptr, WENC_EHIP, "wenc_create: table upload: %s", hipGetErrorString(e));
         }
     }
@@ -957,13 +984,14 @@ int wenc_log_mel(wenc_t *h, const float *audio, int32_t batch, float *mel, void 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const float *tab = reinterpret_cast<const float *>(h->farena);
     const float *win = reinterpret_cast<const float *>(h->farena + h->f_win);
-    const float *filt = reinterpret_cast<const float *>(h->farena + h->f_filt);
+    const float *mwt = reinterpret_cast<const float *>(h->farena + h->f_mwt);
+    const int *mstart = reinterpret_cast<const int *>(h->farena + h->f_mstart);
     float *blk = reinterpret_cast<float *>(h->farena + h->f_blk);
     for (int b0 = 0; b0 < batch; b0 += c.max_batch) {
         const int nb = batch - b0 < c.max_batch ? batch - b0 : c.max_batch;
         WENC_TRY(h->site(WENC_SITE_MEL, st, [&] {
-            return wk::launch_logmel(audio + size_t(b0) * c.n_frames * 160, nb, c.n_frames, tab, win, filt, c.n_mels,
-                                     mel + size_t(b0) * c.n_frames * c.n_mels, blk, st);
+            return wk::launch_logmel(audio + size_t(b0) * c.n_frames * 160, nb, c.n_frames, tab, win, mwt, mstart,
+                                     h->f_nch, c.n_mels, mel + size_t(b0) * c.n_frames * c.n_mels, blk, st);
         }));
     }
     return WENC_OK;
