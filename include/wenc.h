@@ -345,6 +345,17 @@ int wenc_k_gemm_mode(int32_t tile, int32_t split);
 int wenc_k_gemm_plan(int32_t M, int32_t N, int32_t cus, int32_t tile, int32_t split, int32_t streams,
                      int32_t *big_rows);
 
+/* Test-only, host logic (no device work): the mel-filter tables wenc_log_mel
+ * reads for n_mels filters (CKE page, "The Frontend": area-normalised
+ * triangles on the Slaney scale over 0 .. 8 kHz at the 201 bins k * 40 Hz).
+ * Filter m is a window of 16 * (*nch) bins starting at mstart[m], inside bins
+ * 0 .. 200, whose weights are mwt[m][0 .. 16 nch), zero outside the
+ * triangle.  Writes *nch; fills mstart [n_mels] and mwt (row-major, capacity
+ * mwt_cap floats) when both are non-NULL.  WENC_EINVAL when wenc_log_mel
+ * would refuse n_mels (not a multiple of 8 in 8 .. 128), nch is NULL or
+ * mwt_cap is too small. */
+int wenc_k_logmel_tables(int32_t n_mels, int32_t *nch, int32_t *mstart, float *mwt, int64_t mwt_cap);
+
 /* Non-causal attention per (batch, head) (kernels.nu, wk_attn with causal 0):
  *   ao[b][t][h*64 + e] = sum_u softmax_u(q[b][h][t] . k[b][h][u]) * v[b][h][u][e]
  * with q ALREADY scaled by log2(e)/sqrt(64) (the softmax is taken in base 2),

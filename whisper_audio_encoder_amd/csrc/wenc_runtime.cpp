@@ -1067,6 +1067,20 @@ int wenc_k_gemm_plan(int32_t M, int32_t N, int32_t cus, int32_t tile, int32_t sp
     return p.kind;
 }
 
+int wenc_k_logmel_tables(int32_t n_mels, int32_t *nch, int32_t *mstart, float *mwt, int64_t mwt_cap) {
+    if (const char *m = wk::logmel_check(1, 2, n_mels)) return fail(nullptr, WENC_EINVAL, "logmel tables: %s", m);
+    if (!nch) return fail(nullptr, WENC_EINVAL, "logmel tables: nch is NULL");
+    const FrontendTables t = frontend_tables(n_mels);
+    *nch = t.nch;
+    if (!mstart || !mwt) return WENC_OK;
+    if (mwt_cap < int64_t(t.mwt.size()))
+        return fail(nullptr, WENC_EINVAL, "logmel tables: mwt holds %lld floats, %zu needed", (long long)mwt_cap,
+                    t.mwt.size());
+    std::copy(t.mstart.begin(), t.mstart.end(), mstart);
+    std::copy(t.mwt.begin(), t.mwt.end(), mwt);
+    return WENC_OK;
+}
+
 int wenc_k_attention(const uint16_t *q, const uint16_t *k, const uint16_t *vt, uint16_t *ao, int32_t batch,
                      int32_t n_head, int32_t T, int32_t ldvt, void *stream) {
     if (const char *m = wk::attention_check(batch, n_head, T, ldvt)) return fail(nullptr, WENC_EINVAL, "%s", m);

@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
     L.wenc_cross_attend.restype = ctypes.c_int
     L.wenc_k_gemm_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32)]
     L.wenc_k_gemm_plan.restype = ctypes.c_int
+    L.wenc_k_logmel_tables.argtypes = [i32, ctypes.POINTER(i32), vp, vp, ctypes.c_int64]
+    L.wenc_k_logmel_tables.restype = ctypes.c_int
     L.wenc_argmax.argtypes = [vp, vp, i32, i32, ctypes.c_int64, vp, vp]
     L.wenc_argmax.restype = ctypes.c_int
     L.wenc_argmax_noalloc.argtypes = [vp, i32, i32, ctypes.c_int64, vp, vp]
@@ -205,6 +207,21 @@ def wenc_prepare_cross(h, memory: torch.Tensor, batch: int, n_ctx: int, xk: torc
 def wenc_cross_attend(h, q: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, batch: int, n_q: int, n_ctx: int,
                       out: torch.Tensor, stream=None) -> None:
     _check(lib().wenc_cross_attend(h, _ptr(q), _ptr(xk), _ptr(xv), batch, n_q, n_ctx, _ptr(out), _stream(stream)), h)
+
+
+def wenc_k_logmel_tables(n_mels: int):
+    """Host-side mel-filter tables of wenc_log_mel: (mstart [n_mels] int32,
+    mwt [n_mels][16 nch] fp32), see wenc.h."""
+    import numpy as np
+    nch = ctypes.c_int32()
+    if lib().wenc_k_logmel_tables(n_mels, ctypes.byref(nch), None, None, 0) != WENC_OK:
+        raise ValueError(f"wenc_k_logmel_tables: {wenc_last_error()}")
+    mstart = np.zeros(n_mels, dtype=np.int32)
+    mwt = np.zeros((n_mels, 16 * nch.value), dtype=np.float32)
+    rc = lib().wenc_k_logmel_tables(n_mels, ctypes.byref(nch), mstart.ctypes.data, mwt.ctypes.data, mwt.size)
+    if rc != WENC_OK:
+        raise ValueError(f"wenc_k_logmel_tables: {wenc_last_error()}")
+    return mstart, mwt
 
 
 def wenc_k_gemm_plan(M: int, N: int, cus: int = 256, tile: int = -1, split: int = 1,
