@@ -136,6 +136,23 @@ def test_gemm_gelu_f16(M, N, K):
     np.testing.assert_allclose(host(C)[rows].astype(np.float64), ref, rtol=1e-3, atol=1e-4)
 
 
+@pytest.mark.parametrize("M,N,K,ldc", [(300, 132, 240, 132), (70, 4, 64, 4), (300, 384, 64, 400), (513, 256, 128, 264)])
+def test_gemm_gelu_f16_store_layouts(M, N, K, ldc):
+    """The GELU epilogue's two store paths: runs of 8 through one buffer
+    descriptor (N % 8 == 0) and the per-row fallback (N % 8 == 4, whose last
+    run is 4 wide); with ldc > N, and rows past M in the allocation, nothing
+    outside the M x N block is written."""
+    say(f"gemm gelu stores M={M} N={N} K={K} ldc={ldc}")
+    rng = np.random.default_rng(M + 7 * N + K)
+    A, W, b = _operands(rng, M, N, K)
+    C = torch.full((M + 5, ldc), float("nan"), dtype=torch.float16, device=DEV)
+    _gemm(f16_dev(A), f16_dev(W), dev(b), wenc.WENC_EPI_GELU_F16, M, N, K, C=C, ldc=ldc)
+    got = host(C)
+    ref = oracle.gelu(_f64(A) @ _f64(W).T + b)
+    np.testing.assert_allclose(got[:M, :N].astype(np.float64), ref, rtol=1e-3, atol=1e-4)
+    assert np.isnan(got[:M, N:]).all() and np.isnan(got[M:]).all()
+
+
 def test_gemm_gelu_over_its_whole_range():
     """The GELU epilogue at pre-activations spanning [-16, 16] densely
     (every fp16 value there, plus per-column fp32 bias offsets), including the

@@ -55,6 +55,8 @@ struct GemmP {
     DivU c_div;
     int c_off;
     int ldc;
+    int c_run8;  // GELU fp16: rows of C at non-decreasing addresses, N % 8 == 0 and a tile's rows
+                 // within 2 GiB of its first: the epilogue stores through one buffer descriptor
     const float *pos;
     DivU pos_div;
     f16 *q, *k, *vt;
@@ -510,6 +512,8 @@ gemm_kernel(const GemmP p) {
         }
         return;
     }
+    // GELU fp16 output: C from the tile's first row on (its batch item cb0, row cr0)
+    const uint32_t cb0 = divu(uint32_t(m0), p.c_div), cr0 = uint32_t(m0) - cb0 * p.c_div.d;
 #pragma unroll
     for (int cg = 0; cg < WN / 64; ++cg) {
         const int nw = n0 + wn * WN + cg * 64;  // first column of this 64-column group
@@ -591,12 +595,41 @@ gemm_kernel(const GemmP p) {
                 // 8 lanes per 64-half row, 8 rows per instruction
                 const int c = lane & 7, r8 = lane >> 3;
                 const int n = nw + c * 8;
+                bool stored = false;
+                if constexpr (EPI == WENC_EPI_GELU_F16) {
+                    if (p.c_run8) {
+                        const __amdgpu_buffer_rsrc_t rcg = __builtin_amdgcn_make_buffer_rsrc(
+                            static_cast<f16 *>(p.C) + int64_t(cb0) * p.c_bs + (int64_t(cr0) + p.c_off) * p.ldc, 0,
+                            0x7fffffff, 0x00020000);
+                        // All four rows read back first, then four buffer
+                        // stores whose offset is past the range for rows at or
+                        // beyond M and columns at or beyond N (the store is
+                        // dropped): no branch around a store, no 64-bit address
+                        // arithmetic per row, offsets from the tile's first row.
+                        f16x8 o[4];
 #pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    const int r = it * 8 + r8;
-                    const f16x8 o = *reinterpret_cast<const f16x8 *>(stg + (r * RS + c * 8) * 2);
-                    const int m = mr + r;
-                    if (m < p.M && n < p.N) epi_row8<EPI>(p, m, n, o);
+                        for (int it = 0; it < 4; ++it)
+                            o[it] = *reinterpret_cast<const f16x8 *>(stg + ((it * 8 + r8) * RS + c * 8) * 2);
+#pragma unroll
+                        for (int it = 0; it < 4; ++it) {
+                            const int m = mr + it * 8 + r8;
+                            const uint32_t bi = divu(uint32_t(m), p.c_div);
+                            const int64_t e = int64_t(bi - cb0) * p.c_bs +
+                                              (int64_t(uint32_t(m) - bi * p.c_div.d) - int64_t(cr0)) * p.ldc + n;
+                            const uint32_t off = (m < p.M && n < p.N) ? uint32_t(e * 2) : OOB;
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o[it]), rcg, off, 0, 0);
+                        }
+                        stored = true;
+                    }
+                }
+                if (!stored) {
+#pragma unroll
+                    for (int it = 0; it < 4; ++it) {
+                        const int r = it * 8 + r8;
+                        const f16x8 o = *reinterpret_cast<const f16x8 *>(stg + (r * RS + c * 8) * 2);
+                        const int m = mr + r;
+                        if (m < p.M && n < p.N) epi_row8<EPI>(p, m, n, o);
+                    }
                 }
             }
         }
@@ -743,6 +776,15 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag, int cu_d
     p.c_div = make_divu(a.c_rows_per_batch > 0 ? a.c_rows_per_batch : 1);
     p.c_off = a.c_row_offset;
     p.ldc = a.ldc;
+    if (a.epilogue == WENC_EPI_GELU_F16) {
+        // a row's offset from its tile's first row is non-negative when batch
+        // items do not overlap, and below 2 GiB when a tile's 256 rows (which
+        // span at most 256 / D + 2 items of D rows) stay within it
+        const int64_t D = a.c_rows_per_batch;
+        const bool ordered = D >= a.M || a.c_batch_stride >= D * a.ldc;
+        const int64_t span = (256 / D + 2) * a.c_batch_stride + (256 + int64_t(a.c_row_offset)) * a.ldc + a.N;
+        p.c_run8 = a.N % 8 == 0 && a.c_row_offset >= 0 && ordered && span * 2 < (int64_t(1) << 31);
+    }
     p.pos = a.pos;
     p.pos_div = make_divu(a.pos_rows > 0 ? a.pos_rows : 1);
     p.q = reinterpret_cast<f16 *>(a.q);
