@@ -57,6 +57,7 @@ struct GemmP {
     int ldc;
     int c_run8;  // GELU fp16: rows of C at non-decreasing addresses, N % 8 == 0 and a tile's rows
                  // within 2 GiB of its first: the epilogue stores through one buffer descriptor
+    int qk_run8; // QKV: a tile's q and k rows within 2 GiB of its first row's: the same
     const float *pos;
     DivU pos_div;
     f16 *q, *k, *vt;
@@ -622,6 +623,31 @@ gemm_kernel(const GemmP p) {
                         stored = true;
                     }
                 }
+                if constexpr (EPI == WENC_EPI_QKV) {
+                    if (p.qk_run8) {
+                        // q or k of head hq, [b][h][t][64]: key t of batch item b
+                        // is 128 bytes at ((b H + hq) T + t) 64; a pad row (t at
+                        // or past T) or a row at or past M gets an out-of-range
+                        // offset, so the store is dropped
+                        const int sl = nw / p.dmodel, hq = (nw - sl * p.dmodel) >> 6;
+                        const uint32_t qb0 = divu(uint32_t(m0), p.t_div), qt0 = uint32_t(m0) - qb0 * p.t_div.d;
+                        const __amdgpu_buffer_rsrc_t rqk = __builtin_amdgcn_make_buffer_rsrc(
+                            (sl == 0 ? p.q : p.k) + ((int64_t(qb0) * p.H + hq) * p.T + qt0) * 64, 0, 0x7fffffff, 0x00020000);
+                        f16x8 o[4];
+#pragma unroll
+                        for (int it = 0; it < 4; ++it)
+                            o[it] = *reinterpret_cast<const f16x8 *>(stg + ((it * 8 + r8) * RS + c * 8) * 2);
+#pragma unroll
+                        for (int it = 0; it < 4; ++it) {
+                            const int m = mr + it * 8 + r8;
+                            const uint32_t bb = divu(uint32_t(m), p.t_div), t = uint32_t(m) - bb * p.t_div.d;
+                            const int64_t e = (int64_t(bb - qb0) * p.H * p.T + (int64_t(t) - int64_t(qt0))) * 64 + c * 8;
+                            const uint32_t off = (m < p.M && t < uint32_t(p.T) && n < p.N) ? uint32_t(e * 2) : OOB;
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o[it]), rqk, off, 0, 0);
+                        }
+                        stored = true;
+                    }
+                }
                 if (!stored) {
 #pragma unroll
                     for (int it = 0; it < 4; ++it) {
@@ -812,6 +838,8 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag, int cu_d
         p.a_bs = int64_t(a.T) * a.lda;
         p.a_valid = a.T;
         p.t_div = make_divu(tp);
+        // a tile's 256 rows span at most 256 / tp + 2 batch items of H T keys of 64
+        p.qk_run8 = (int64_t(256 / tp + 2) * a.n_head * a.T + 256) * 64 * 2 < (int64_t(1) << 31);
     }
     const int tile = tile_mode().tile.load(), split = tile_mode().split.load();
     const GemmPlan plan = gemm_plan(p.M, p.N, cu_count(), tile == 0 || tile == 1 ? tile : -1, split, std::max(cu_div, 1));
