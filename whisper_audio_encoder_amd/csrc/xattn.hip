@@ -11,13 +11,13 @@
 // describes the remedy its one-query kernel uses: split the keys across
 // workgroups and merge the partial softmaxes.  The layout below is our own.
 //
-// Pass 1 (xattn_partial): a workgroup takes 64 keys per wave of one (b, h); each
-// lane scores one key against every query (the key row, 128 bytes, in
-// registers; dot products as fp16 pairs accumulated in fp32), a wave takes
-// its maximum and exp2 sum, then accumulates P.V with 8 lanes per value row
-// (8 dimensions each; the rows were loaded before the scores); the
-// waves merge through LDS and write the workgroup's (max, sum, o[64]) per
-// query.  Pass 2
+// Pass 1 (xattn_partial): a workgroup takes 64 keys per wave of one (b, h);
+// K and V rows are read 8 lanes to a row (16 bytes a lane), the partial dot
+// products of a key's 8 lanes (fp16 pairs accumulated in fp32) are summed by
+// a reduce-scatter that leaves one key's score per lane, a wave takes its
+// maximum and exp2 sum, then accumulates P.V with the same 8 lanes per value
+// row; the waves merge through LDS and write the workgroup's (max, sum,
+// o[64]) per query.  Pass 2
 // (xattn_merge): one wave per (b, h) rescales the partials to a common
 // maximum and sums them in key order, so the result does not depend on
 // scheduling.  The work is bound by reading K and V once (HBM).
@@ -66,46 +66,63 @@ xattn_partial(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *
     }
     __syncthreads();
 
-    // scores: lane = one key of this wave's 64 (base-2, scaled by log2(e)/8).
-    // The wave's 64 value rows are loaded up front (lane: rows 8 it + (lane
-    // >> 3), dimensions 8 (lane & 7) .. +7), so they are in flight while the
-    // scores are formed.
+    // K and V rows are both read 8 lanes to a row: in load it, lane (r8 =
+    // lane >> 3, dq = lane & 7) holds dimensions 8 dq .. +7 of key 8 it + r8,
+    // so one instruction covers 8 whole 128-byte rows.  The loads are buffer
+    // loads over this window's K and V (a key at or past T has an offset past
+    // the range and reads zero), all issued before the scores, K first.
     const int key0 = c * XKC + wave * 64;
-    const int u = key0 + lane;
     const int dq = lane & 7, r8 = lane >> 3;
-    f16x8 vv[8];
+    const uint32_t range = uint32_t(T) * uint32_t(d) * 2u;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<f16 *>(xk) + int64_t(b) * T * d, 0, int(range), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<f16 *>(xv) + int64_t(b) * T * d, 0, int(range), 0x00020000);
+    f16x8 kv[8], vv[8];
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
         const int uu = key0 + 8 * it + r8;
-        vv[it] = uu < T ? *reinterpret_cast<const f16x8 *>(xv + (int64_t(b) * T + uu) * d + h * 64 + 8 * dq)
-                        : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        const uint32_t off = uu < T ? uint32_t((int64_t(uu) * d + h * 64 + 8 * dq) * 2) : 0x80000000u;
+        kv[it] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
     }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int uu = key0 + 8 * it + r8;
+        const uint32_t off = uu < T ? uint32_t((int64_t(uu) * d + h * 64 + 8 * dq) * 2) : 0x80000000u;
+        vv[it] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    }
+    // scores (base 2, scaled by log2(e)/8): each lane's partial dot product
+    // over its 8 dimensions, then a reduce-scatter over the 8 lanes of a row
+    // (exchanging 4, 2, 1 partials with lanes dq ^ 4, ^ 2, ^ 1), after which
+    // lane (r8, dq) holds the whole score of key u = 8 dq + r8.
+    const int u = key0 + 8 * dq + r8;
     float s[NQ];
-    if (u < T) {
-        const f16 *kr = xk + (int64_t(b) * T + u) * d + h * 64;
-        f16x8 kv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) kv[j] = *reinterpret_cast<const f16x8 *>(kr + 8 * j);
+    for (int i = 0; i < NQ; ++i) {
+        float v8[8];
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) {
+        for (int it = 0; it < 8; ++it) {
             float acc = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    acc = __builtin_amdgcn_fdot2(f16x2{kv[j][2 * t], kv[j][2 * t + 1]}, qs[i][4 * j + t], acc, false);
-            s[i] = acc * LOG2E_8;
+            for (int t = 0; t < 4; ++t)
+                acc = __builtin_amdgcn_fdot2(f16x2{kv[it][2 * t], kv[it][2 * t + 1]}, qs[i][4 * dq + t], acc, false);
+            v8[it] = acc;
         }
-    } else {
+        float v4[4], v2[2];
+        const bool b4 = dq & 4, b2 = dq & 2, b1 = dq & 1;
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) s[i] = -INFINITY;
+        for (int j = 0; j < 4; ++j) v4[j] = (b4 ? v8[j + 4] : v8[j]) + __shfl_xor(b4 ? v8[j] : v8[j + 4], 4);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) v2[j] = (b2 ? v4[j + 2] : v4[j]) + __shfl_xor(b2 ? v4[j] : v4[j + 2], 2);
+        const float full = (b1 ? v2[1] : v2[0]) + __shfl_xor(b1 ? v2[0] : v2[1], 1);
+        s[i] = u < T ? full * LOG2E_8 : -INFINITY;
     }
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
         const float m = wave_max(s[i]);  // -inf only when every key of the wave is past T
         const float p = u < T ? __builtin_amdgcn_exp2f(s[i] - m) : 0.f;
         const float l = wave_add(p);
-        ps[wave][i][lane] = p;
+        ps[wave][i][8 * dq + r8] = p;
         if (lane == 0) {
             wm[wave][i] = m;
             wl[wave][i] = l;
@@ -210,6 +227,7 @@ const char *xattn_check(int batch, int n_head, int n_q, int T) {
     if (batch < 0 || n_head <= 0) return "cross attention: need batch >= 0, n_head > 0";
     if (n_q < 1 || n_q > XATTN_MAX_Q) return "cross attention: n_q must be in [1, 8]";
     if (T < 1) return "cross attention: n_ctx must be >= 1";
+    if (int64_t(T) * n_head * 64 * 2 >= (int64_t(1) << 31)) return "cross attention: a window's K or V exceeds 2 GiB";
     if (int64_t(batch) * n_head * ((T + XKC - 1) / XKC) >= (int64_t(1) << 31)) return "cross attention: grid too large";
     return nullptr;
 }
