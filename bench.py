@@ -152,6 +152,49 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": 5}), flush=True)
 
 
+def hbm_ceiling(steps=50):
+    """The LayerNorm against plain conversions that move the same bytes: per
+    shape (24000 x 1280 and 24000 x 768, the encoder's rows at d 1280 and
+    768), an fp32 -> fp16 conversion by torch (reads 4 and writes 2 bytes per
+    element, as the LayerNorm does), an fp32 copy of the same number of
+    bytes moved, and the library's LayerNorm.  Prints one JSON line of
+    achieved GB/s (bytes read + written over the average launch time)."""
+    import torch
+    from whisper_audio_encoder_amd import wenc
+
+    def rate(fn, nbytes):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        return {"us": round(us, 2), "GB_per_s": round(nbytes / us / 1e3, 1)}
+
+    out = {}
+    g = torch.Generator(device="cuda:0").manual_seed(5)
+    for rows, d in ((24000, 1280), (24000, 768)):
+        n = rows * d
+        x = torch.randn(rows, d, device="cuda:0", generator=g)
+        y16 = torch.empty(rows, d, device="cuda:0", dtype=torch.half)
+        gam = torch.ones(d, device="cuda:0")
+        bet = torch.zeros(d, device="cuda:0")
+        c_src = torch.empty(n * 6 // 8, device="cuda:0")  # fp32 copy moving 6 bytes per element
+        c_dst = torch.empty_like(c_src)
+        out[f"{rows}x{d}"] = {
+            "bytes": 6 * n,
+            "torch_fp32_to_fp16": rate(lambda: y16.copy_(x), 6 * n),
+            "torch_fp32_copy": rate(lambda: c_dst.copy_(c_src), 6 * n),
+            "layernorm": rate(lambda: wenc.wenc_k_layernorm(x, gam, bet, y16, rows, d, 1e-5, False,
+                                                            torch.cuda.current_stream()), 6 * n),
+        }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(cfg, mel, params, budget_s=30.0):
     """Time the fp64 oracle on one window of the workload (all blocks)."""
     import oracle
@@ -507,6 +550,8 @@ def main(argv=None):
                     help="also time the cross-attention K/V projection of N_DEC decoder layers from the output")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="only time the LayerNorm against torch conversions moving the same bytes and exit")
     ap.add_argument("--gemm-tile-costs", action="store_true",
                     help="only measure the 256 x 256 GEMM's cost per k step and per tile and exit")
     a = ap.parse_args(argv)
@@ -515,6 +560,9 @@ def main(argv=None):
         return
     if a.gemm_tile_costs:
         gemm_tile_costs()
+        return
+    if a.hbm_ceiling:
+        hbm_ceiling()
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the encoder shards by window (pure data parallelism, no "
