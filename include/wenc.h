@@ -324,7 +324,10 @@ int wenc_argmax_noalloc(const float *logits, int32_t rows, int32_t n_vocab, int6
 /* Test-only: the tile configuration of every later GEMM launch in this
  * process (all handles).  tile: -1 automatic (the default, or the
  * WENC_GEMM_TILE environment variable when set), 0 = 128 x 128 tiles,
- * 1 = 256 x 256 tiles.  split: 1 (the default) lets an automatic launch give
+ * 1 = 256 x 256 tiles, 2 = 256 x 256 tiles whose main loop runs every wave
+ * in the same phase (the default 256 x 256 main loop runs the two waves of
+ * a SIMD a phase apart, one issuing MFMAs while the other reads LDS).
+ * split: 1 (the default) lets an automatic launch give
  * its last 256-row tile rows to 128 x 128 tiles when that evens out the last
  * round over the compute units, 0 keeps one tile size.  Every configuration
  * sums each output over k in the same order, so all give the same bits.

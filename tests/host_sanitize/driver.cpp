@@ -150,7 +150,7 @@ void planner() {
     CHECK(wenc_k_gemm_plan(64, 64, 256, 2, 1, 1, &big) == WENC_EINVAL);
     CHECK(wenc_k_gemm_plan(64, 64, 256, -1, 1, 0, &big) == WENC_EINVAL);
     CHECK(wenc_k_gemm_plan(64, 64, 256, -1, 1, 1, nullptr) == WENC_EINVAL);
-    CHECK(wenc_k_gemm_mode(2, 1) == WENC_EINVAL && wenc_k_gemm_mode(-1, 5) == WENC_EINVAL);
+    CHECK(wenc_k_gemm_mode(3, 1) == WENC_EINVAL && wenc_k_gemm_mode(-1, 5) == WENC_EINVAL);
     CHECK(wenc_k_gemm_mode(-1, 1) == WENC_OK);
 }
 

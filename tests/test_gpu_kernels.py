@@ -212,8 +212,9 @@ def _gemm_mode(tile, split):
     assert wenc.lib().wenc_k_gemm_mode(tile, split) == wenc.WENC_OK
 
 
-# automatic with the last tile rows split off, automatic without, all 256 x 256, all 128 x 128
-GEMM_MODES = [(-1, 1), (-1, 0), (1, 0), (0, 0)]
+# automatic with the last tile rows split off, automatic without, all 256 x 256, all 256 x 256 with
+# the lockstep main loop, all 128 x 128
+GEMM_MODES = [(-1, 1), (-1, 0), (1, 0), (2, 0), (0, 0)]
 
 
 @pytest.mark.parametrize("epi", [wenc.WENC_EPI_GELU_F16, wenc.WENC_EPI_RESID])
@@ -248,11 +249,12 @@ def test_gemm_tile_configs_bitwise(epi):
 
 @pytest.mark.parametrize("K", [64, 128, 192, 256, 320, 384, 448, 704, 776])
 def test_gemm_every_pipeline_depth(K):
-    """The operand pipeline (A fetched three k-steps ahead through three LDS
-    buffers, W two through two, the loop unrolled by six) for 1, 2, 3, 4, 5,
-    6, 7 and 11 k-steps and 13 with a ragged K tail (776 = 12 x 64 + 8), so
-    the loop leaves at each of its six positions, on both tile sizes: the
-    fp64 sums within fp32 accumulation, and both tile sizes the same bits."""
+    """The operand pipelines (three LDS buffers for A and two for W, the
+    loops unrolled by six; the 128 x 128 and lockstep 256 x 256 loops fetch A
+    three k-steps ahead and W two, the ping-pong 256 x 256 loop A two and W
+    one) for 1, 2, 3, 4, 5, 6, 7 and 11 k-steps and 13 with a ragged K tail
+    (776 = 12 x 64 + 8), so each loop leaves at each of its six positions:
+    the fp64 sums within fp32 accumulation, and all three the same bits."""
     M, N = 600, 640
     say(f"gemm pipeline depth K={K}")
     rng = np.random.default_rng(K)
@@ -261,14 +263,15 @@ def test_gemm_every_pipeline_depth(K):
     x0 = rng.standard_normal((M, N)).astype(np.float32)
     outs = []
     try:
-        for tile in (0, 1):
+        for tile in (0, 1, 2):
             _gemm_mode(tile, 0)
             C = dev(x0)
             _gemm(Ad, Wd, bd, wenc.WENC_EPI_RESID, M, N, K, C=C)
             outs.append(host(C))
     finally:
         _gemm_mode(-1, 1)
-    assert np.array_equal(outs[0], outs[1])
+    for o in outs[1:]:
+        assert np.array_equal(outs[0], o)
     np.testing.assert_allclose(outs[0], x0 + _f64(A) @ _f64(W).T + b, rtol=1e-5, atol=1e-4)
 
 
@@ -305,7 +308,8 @@ def test_gemm_qkv_tile_configs_bitwise():
 
 def test_gemm_mode_rejects_bad_values():
     L = wenc.lib()
-    assert L.wenc_k_gemm_mode(2, 1) == wenc.WENC_EINVAL
+    assert L.wenc_k_gemm_mode(3, 1) == wenc.WENC_EINVAL
+    assert L.wenc_k_gemm_mode(-2, 1) == wenc.WENC_EINVAL
     assert L.wenc_k_gemm_mode(-1, 2) == wenc.WENC_EINVAL
     assert L.wenc_k_gemm_mode(-1, 1) == wenc.WENC_OK
 

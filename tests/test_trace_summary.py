@@ -12,6 +12,10 @@ def test_site_of_kernel_names():
     assert ts.site_of(g.format(e=2, t=0)) == "oproj"
     assert ts.site_of(g.format(e=2, t=1)) == "fc2"
     assert ts.site_of(g.format(e=3, t=0)) == "qkv"
+    g8 = "void wk::(anonymous namespace)::gemm_kernel<256, 256, 128, 64, 8, {e}, {t}, {pp}>(wk::(anonymous namespace)::GemmP)"
+    assert ts.site_of(g8.format(e=0, t=1, pp=1)) == "fc1"
+    assert ts.site_of(g8.format(e=2, t=1, pp=0)) == "fc2"
+    assert ts.site_of(g8.format(e=4, t=0, pp=1)) == "xkv"
     assert ts.site_of("_ZN2wk12_GLOBAL__N_111attn_kernelEPKDF16_S2_S2_PDF16_iii") == "attn"
     assert ts.site_of("void wk::(anonymous namespace)::ln_kernel<5, false>(float const*)") == "ln"
     assert ts.site_of("void wk::(anonymous namespace)::ln_kernel<5, true>(float const*)") == "lnf"

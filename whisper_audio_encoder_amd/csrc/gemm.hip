@@ -18,9 +18,12 @@
 // and K tails without branches.  Within LDS, 16-byte chunks are XOR-swizzled
 // by row so that fragment reads are free of bank conflicts; the direct loads
 // produce that layout by choosing which global chunk each lane fetches.  The
-// A part of a step has three LDS buffers and the W part two, so A transfers
-// are issued three steps ahead of their use and W transfers two, with one
-// barrier per step.  The MFMA takes W as its A operand and A^T as its B operand, so
+// A part of a step has three LDS buffers and the W part two.  The 128 x 128
+// kernel issues A transfers three steps ahead of their use and W transfers
+// two, with one barrier per step.  The 256 x 256 kernel runs a ping-pong
+// schedule: the two waves sharing a SIMD work a phase apart, one issuing a
+// step's MFMAs while the other reads its fragments from LDS and issues
+// transfers (details at the main loop).  The MFMA takes W as its A operand and A^T as its B operand, so
 // each lane ends up owning one output row and runs of 4 consecutive output
 // columns, which the epilogues store as 8- or 16-byte vectors.
 //
@@ -194,7 +197,7 @@ __device__ __forceinline__ void epi_row8(const GemmP &p, int m, int n, f16x8 o) 
 // 128 x 128 kernel is held to two workgroups per CU (its LDS allows two).
 // (A 4-wave 256 x 256 kernel with 128 x 128 per wave, accumulators in
 // AGPRs, compiles from this template too; it measured 10-20% slower.)
-template <int BM, int BN, int WM, int WN, int NW, int EPI, int TAG>
+template <int BM, int BN, int WM, int WN, int NW, int EPI, int TAG, int PP>
 __global__ void __launch_bounds__(NW * 64, (NW >= 8 || BM >= 256) ? 1 : 2)
 gemm_kernel(const GemmP p) {
     constexpr int WAVES_N = BN / WN;
@@ -322,6 +325,164 @@ gemm_kernel(const GemmP p) {
     // step kt+3 go into the buffers step kt has just released.  (The last
     // step's slice 1 reads idle buffers; those fragments are not used.)
     const int nk = (p.K + BK - 1) / BK;
+    if constexpr (PP) {
+        static_assert(BM == 256 && BN == 256 && WM == 128 && WN == 64 && NW == 8, "ping-pong: 256 x 256, 8 waves");
+        // Ping-pong schedule.  Wave w runs on SIMD w % 4, so waves w and
+        // w + 4 share a SIMD: group 0 (waves 0..3, tile rows 0..127) and
+        // group 1 (waves 4..7, rows 128..255) have one wave on each SIMD.
+        // Every wave runs the same loop, per k step j: a memory phase (its
+        // share of a later step's direct loads, then the fragments of step
+        // j from LDS), a barrier, a compute phase (the step's 64 MFMAs), a
+        // barrier.  Group 1 passes one extra barrier before the loop, so
+        // its phases run one slot behind group 0's: while one wave of a
+        // SIMD issues MFMAs, the other's LDS reads are in flight.  Step j
+        // is read by group 0 in slot 2j and by group 1 in slot 2j + 1.
+        // Group 0 moves W: in its memory phase of step j, W of step j + 1
+        // into the W buffer step j - 1 has freed; it waits for it after its
+        // compute phase of step j.  Group 1 moves A: in its memory phase of
+        // step j, A of step j + 2 into the A buffer step j - 1 has freed;
+        // it waits for A of step j + 1 at the end of that phase.  Either
+        // way a step's data has landed before the barrier that opens slot
+        // 2j, where group 0 first reads it.  The compute phase reads the A
+        // side of the second k slice itself (see pcomp).
+        const int grp = wm;
+        const int lw4 = wave & 3;
+        uint32_t poff[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const int r = (lw4 * 8 + g) * 8 + (lane >> 3);
+            const uint32_t ch = uint32_t((lane & 7) ^ swz(r));
+            uint32_t off;
+            if (grp == 0) {
+                off = n0 + r < p.N ? uint32_t(r * p.ldw * 2) + ch * 16 : OOB;
+            } else {
+                const int m = m0 + r;
+                const bool ok = m < p.M && int(m - divu(m, p.a_div) * p.a_div.d) < p.a_valid;
+                off = ok ? uint32_t((a_row(p, m) - a0) * 2) + ch * 16 : OOB;
+            }
+            poff[g] = off;
+        }
+        const i32x4 prs = grp == 0 ? rb : ra;
+        // this wave's share of its group's operand for step kt, into the
+        // LDS buffer at byte address st
+        auto pissue = [&](int kt, uint32_t st) __attribute__((always_inline)) {
+            const uint32_t kb = uint32_t(kt) * (BK * 2);
+            if ((kt + 1) * BK <= p.K) {
+#pragma unroll
+                for (int g = 0; g < 8; ++g) load_lds16(prs, st + (lw4 * 8 + g) * 8 * BK * 2, poff[g] + kb);
+            } else {
+#pragma unroll
+                for (int g = 0; g < 8; ++g) {
+                    const int r = (lw4 * 8 + g) * 8 + (lane >> 3);
+                    const int ch = (lane & 7) ^ swz(r);
+                    const uint32_t kflag = (kt * BK + ch * 8 < p.K) ? 0u : OOB;
+                    load_lds16(prs, st + (lw4 * 8 + g) * 8 * BK * 2, (poff[g] | kflag) + kb);
+                }
+            }
+        };
+        // Fragments: the memory phase reads the A side of slice 0 and the W
+        // side of both slices; the compute phase reads the A side of slice 1
+        // into the registers of slice 0's, block row by block row, as soon
+        // as that row's slice-0 MFMAs are issued (a wave holds one A-side
+        // set: the registers of a whole step's fragments would not fit).
+        f16x8 pa[TM], pb0[TN], pb1[TN];
+        const int pch0 = ((lane >> 4) ^ fsw) << 3, pch1 = ((4 + (lane >> 4)) ^ fsw) << 3;
+        auto pmem = [&](const f16 *asrc, const f16 *wsrc) __attribute__((always_inline)) {
+            const f16 *as = asrc + (wm * WM + frow) * BK;
+            const f16 *bs = wsrc + (wn * WN + frow) * BK;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) pa[i] = *reinterpret_cast<const f16x8 *>(as + i * 16 * BK + pch0);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                pb0[j] = *reinterpret_cast<const f16x8 *>(bs + j * 16 * BK + pch0);
+                pb1[j] = *reinterpret_cast<const f16x8 *>(bs + j * 16 * BK + pch1);
+            }
+        };
+        auto pcomp = [&](const f16 *asrc) __attribute__((always_inline)) {
+            const f16 *as = asrc + (wm * WM + frow) * BK;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pb0[j], pa[i], acc[i][j], 0, 0, 0);
+                pa[i] = *reinterpret_cast<const f16x8 *>(as + i * 16 * BK + pch1);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pb1[j], pa[i], acc[i][j], 0, 0, 0);
+        };
+        const f16 *A0 = smem0, *A1 = smem1, *A2 = smemA2, *W0 = smem0 + ASZ, *W1 = smem1 + ASZ;
+        const uint32_t la0 = lds_addr(smem0), la1 = lds_addr(smem1), la2 = lds_addr(smemA2);
+        const uint32_t lw0 = la0 + ASZ * 2, lw1 = la1 + ASZ * 2;
+        // prologue: W of step 0 (group 0), A of steps 0 and 1 (group 1)
+        if (grp == 0) {
+            pissue(0, lw0);
+        } else {
+            pissue(0, la0);
+            if (nk > 1) pissue(1, la1);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(bias[j]));
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = n0 + wn * WN + j * 16 + 4 * hh;
+            const f32x4 b = n < p.N ? bias[j] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < TM; ++i) acc[i][j] = b;
+        }
+        __syncthreads();
+        if (grp == 1) __builtin_amdgcn_s_barrier();  // group 1 one slot behind
+        // step j: A in buffer a_j, W in w_j; group 0 moves W of step j + 1
+        // to wst, group 1 A of step j + 2 to ast
+        auto pstep = [&](int j, const f16 *a_j, const f16 *w_j, uint32_t wst, uint32_t ast)
+                         __attribute__((always_inline)) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (grp == 0) {
+                if (j + 1 < nk) pissue(j + 1, wst);
+            } else {
+                if (j + 2 < nk) pissue(j + 2, ast);
+            }
+            pmem(a_j, w_j);
+            __builtin_amdgcn_sched_barrier(0);
+            if (grp == 1) {
+                if (j + 2 < nk)
+                    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            pcomp(a_j);
+            __builtin_amdgcn_sched_barrier(0);
+            if (grp == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        };
+        // unrolled by six (A period 3, W period 2) so every LDS access names
+        // its buffer statically
+#pragma unroll 1
+        for (int kt = 0; kt < nk; kt += 6) {
+            pstep(kt, A0, W0, lw1, la2);
+            if (kt + 1 >= nk) break;
+            pstep(kt + 1, A1, W1, lw0, la0);
+            if (kt + 2 >= nk) break;
+            pstep(kt + 2, A2, W0, lw1, la1);
+            if (kt + 3 >= nk) break;
+            pstep(kt + 3, A0, W1, lw0, la2);
+            if (kt + 4 >= nk) break;
+            pstep(kt + 4, A1, W0, lw1, la0);
+            if (kt + 5 >= nk) break;
+            pstep(kt + 5, A2, W1, lw0, la1);
+        }
+        if (grp == 0) __builtin_amdgcn_s_barrier();  // match group 1's extra barrier
+    } else {
     f16x8 af[TM], bf0[TN], bf1[TN];
     auto slice = [&](const f16x8 (&bfc)[TN], f16x8 (&bfn)[TN], const f16 *asrc, const f16 *wsrc, int kk)
                      __attribute__((always_inline)) {
@@ -416,6 +577,7 @@ gemm_kernel(const GemmP p) {
         step(kt + 4, A1, W0, A2, W1, la1, lw0);
         if (kt + 5 >= nk) break;
         step(kt + 5, A2, W1, A0, W0, la2, lw1);
+    }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -662,31 +824,10 @@ gemm_kernel(const GemmP p) {
     }
 }
 
-template <int BM, int BN, int WM, int WN, int NW, int TAG>
-hipError_t launch_cfg(const GemmP &base, int epi, hipStream_t s) {
-    GemmP p = base;
-    p.tiles_m = (p.M - p.m_begin + BM - 1) / BM;
-    p.tiles_n = (p.N + BN - 1) / BN;
-    const dim3 grid(p.tiles_m * p.tiles_n), block(NW * 64);
-    switch (epi) {
-        case WENC_EPI_GELU_F16: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_GELU_F16, TAG><<<grid, block, 0, s>>>(p); break;
-        case WENC_EPI_CONV2: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_CONV2, 0><<<grid, block, 0, s>>>(p); break;
-        case WENC_EPI_RESID: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_RESID, TAG><<<grid, block, 0, s>>>(p); break;
-        case WENC_EPI_QKV: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_QKV, 0><<<grid, block, 0, s>>>(p); break;
-        case WENC_EPI_KV: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_KV, 0><<<grid, block, 0, s>>>(p); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
-template <int BM, int BN, int WM, int WN, int NW>
-hipError_t launch_tagged(const GemmP &p, int epi, int tag, hipStream_t s) {
-    return tag ? launch_cfg<BM, BN, WM, WN, NW, 1>(p, epi, s) : launch_cfg<BM, BN, WM, WN, NW, 0>(p, epi, s);
-}
-
 // Tile configuration shared by every launch in the process (a test-only
-// override): tile 0 = 128x128 x 4 waves, 1 = 256x256 x 8 waves, anything
-// else = chosen per launch; split 0 keeps a launch on one tile size.  The
+// override): tile 0 = 128x128 x 4 waves, 1 = 256x256 x 8 waves, 2 = 256x256
+// x 8 waves with the lockstep main loop instead of the ping-pong one,
+// anything else = chosen per launch; split 0 keeps a launch on one tile size.  The
 // environment (WENC_GEMM_TILE, WENC_GEMM_SPLIT) is read once, under the
 // thread-safe initialisation of a function-local static; later changes go
 // through gemm_mode.  Atomics, so launches on other threads read a whole
@@ -706,6 +847,34 @@ TileMode &tile_mode() {
     return m;
 }
 
+template <int BM, int BN, int WM, int WN, int NW, int TAG, int PP>
+hipError_t launch_cfg(const GemmP &base, int epi, hipStream_t s) {
+    GemmP p = base;
+    p.tiles_m = (p.M - p.m_begin + BM - 1) / BM;
+    p.tiles_n = (p.N + BN - 1) / BN;
+    const dim3 grid(p.tiles_m * p.tiles_n), block(NW * 64);
+    switch (epi) {
+        case WENC_EPI_GELU_F16: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_GELU_F16, TAG, PP><<<grid, block, 0, s>>>(p); break;
+        case WENC_EPI_CONV2: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_CONV2, 0, PP><<<grid, block, 0, s>>>(p); break;
+        case WENC_EPI_RESID: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_RESID, TAG, PP><<<grid, block, 0, s>>>(p); break;
+        case WENC_EPI_QKV: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_QKV, 0, PP><<<grid, block, 0, s>>>(p); break;
+        case WENC_EPI_KV: gemm_kernel<BM, BN, WM, WN, NW, WENC_EPI_KV, 0, PP><<<grid, block, 0, s>>>(p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// The 256 x 256 kernel runs the ping-pong main loop unless `lockstep`.
+template <int BM, int BN, int WM, int WN, int NW>
+hipError_t launch_tagged(const GemmP &p, int epi, int tag, hipStream_t s, bool lockstep = false) {
+    if constexpr (BM == 256) {
+        if (!lockstep)
+            return tag ? launch_cfg<BM, BN, WM, WN, NW, 1, 1>(p, epi, s) : launch_cfg<BM, BN, WM, WN, NW, 0, 1>(p, epi, s);
+    }
+    return tag ? launch_cfg<BM, BN, WM, WN, NW, 1, 0>(p, epi, s) : launch_cfg<BM, BN, WM, WN, NW, 0, 0>(p, epi, s);
+}
+
+
 }  // namespace
 
 // Compute units of the current device (cached per device; a race only
@@ -723,7 +892,7 @@ long cu_count() {
 }
 
 int gemm_mode(int tile, int split) {
-    if (tile < -1 || tile > 1 || split < 0 || split > 1) return -1;
+    if (tile < -1 || tile > 2 || split < 0 || split > 1) return -1;
     if (tile == -1) {
         const char *e = std::getenv("WENC_GEMM_TILE");
         tile = e ? std::atoi(e) : 99;
@@ -842,12 +1011,14 @@ hipError_t launch_gemm(const wenc_gemm_args &a, hipStream_t s, int tag, int cu_d
         p.qk_run8 = (int64_t(256 / tp + 2) * a.n_head * a.T + 256) * 64 * 2 < (int64_t(1) << 31);
     }
     const int tile = tile_mode().tile.load(), split = tile_mode().split.load();
-    const GemmPlan plan = gemm_plan(p.M, p.N, cu_count(), tile == 0 || tile == 1 ? tile : -1, split, std::max(cu_div, 1));
+    const bool lockstep = tile == 2;
+    const int plan_tile = tile == 0 || tile == 1 ? tile : (lockstep ? 1 : -1);
+    const GemmPlan plan = gemm_plan(p.M, p.N, cu_count(), plan_tile, split, std::max(cu_div, 1));
     if (plan.kind == GEMM_PLAN_SMALL) return launch_tagged<128, 128, 64, 64, 4>(p, a.epilogue, tag, s);
-    if (plan.kind == GEMM_PLAN_BIG) return launch_tagged<256, 256, 128, 64, 8>(p, a.epilogue, tag, s);
+    if (plan.kind == GEMM_PLAN_BIG) return launch_tagged<256, 256, 128, 64, 8>(p, a.epilogue, tag, s, lockstep);
     GemmP big = p;
     big.M = plan.big_rows;
-    const hipError_t e = launch_tagged<256, 256, 128, 64, 8>(big, a.epilogue, tag, s);
+    const hipError_t e = launch_tagged<256, 256, 128, 64, 8>(big, a.epilogue, tag, s, lockstep);
     if (e != hipSuccess) return e;
     GemmP tail = p;
     tail.m_begin = plan.big_rows;

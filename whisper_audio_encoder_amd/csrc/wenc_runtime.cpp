@@ -1053,7 +1053,7 @@ int wenc_k_gemm(const wenc_gemm_args *args, void *stream) {
 }
 
 int wenc_k_gemm_mode(int32_t tile, int32_t split) {
-    if (wk::gemm_mode(tile, split) != 0) return fail(nullptr, WENC_EINVAL, "gemm mode: tile must be -1, 0 or 1 and split 0 or 1");
+    if (wk::gemm_mode(tile, split) != 0) return fail(nullptr, WENC_EINVAL, "gemm mode: tile must be -1, 0, 1 or 2 and split 0 or 1");
     return WENC_OK;
 }
 

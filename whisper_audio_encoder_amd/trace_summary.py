@@ -23,14 +23,15 @@ from collections import defaultdict
 
 from .configs import CONFIGS
 
-# gemm_kernel<BM, BN, WM, WN, NW, EPI, TAG>: EPI and TAG name the projection
+# gemm_kernel<BM, BN, WM, WN, NW, EPI, TAG, PP>: EPI and TAG name the projection (PP, the main-loop
+# schedule, is absent from traces of earlier builds)
 GEMM_SITES = {(0, 0): "conv1", (0, 1): "fc1", (1, 0): "conv2", (2, 0): "oproj", (2, 1): "fc2", (3, 0): "qkv",
               (4, 0): "xkv"}
 BLOCK_SITES = ("ln", "qkv", "attn", "oproj", "fc1", "fc2")
 
 
 def site_of(name: str) -> str | None:
-    m = re.search(r"gemm_kernel<\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+)>", name)
+    m = re.search(r"gemm_kernel<\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+)(?:,\s*\d+)?>", name)
     if m:
         return GEMM_SITES.get((int(m.group(6)), int(m.group(7))))
     if "attn_kernel" in name:
