@@ -460,8 +460,12 @@ gemm_kernel(const GemmP p) {
             }
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
+            // the compute phase at raised wave priority: the SIMD's other wave,
+            // in its memory phase, then yields the issue slots it contends for
+            __builtin_amdgcn_s_setprio(1);
             pcomp(a_j);
             __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
             if (grp == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         };
