@@ -98,44 +98,52 @@ def gemm_tile_costs(steps=20):
     2048, with the fp16 GELU epilogue and the fp32 residual epilogue.  A
     line fitted to the time per round against the k steps (K >= 256) splits
     it into a cost per 64-wide k step and a fixed cost per tile (prologue and
-    epilogue).  Prints one JSON line."""
+    epilogue).  The same again under light load: M = 1024, N = 2048 (32
+    tiles, one round on 32 compute units, the rest of the chip idle).
+    Prints one JSON line."""
     import numpy as np
     import torch
     from whisper_audio_encoder_amd import wenc
     if wenc.lib().wenc_k_gemm_mode(1, 0) != wenc.WENC_OK:  # 256 x 256 tiles everywhere, no tail split
         raise RuntimeError(wenc.wenc_last_error())
-    M, N = 16384, 4096
-    rounds = M // 256 * (N // 256) / 256
-    out = {"shape": {"M": M, "N": N, "tiles": M // 256 * (N // 256), "rounds_on_256_cus": rounds}}
+    out = {}
+
+    def series(M, N, epi, rounds):
+        pts = []
+        for K in (64, 128, 256, 512, 1024, 2048):
+            A = torch.randn(M, K, device="cuda:0").half()
+            W = (0.02 * torch.randn(N, K, device="cuda:0")).half()
+            b = torch.zeros(N, device="cuda:0")
+            C = (torch.empty(M, N, device="cuda:0", dtype=torch.half) if epi == wenc.WENC_EPI_GELU_F16
+                 else torch.zeros(M, N, device="cuda:0"))
+            g = wenc.wenc_gemm_args()
+            g.A, g.W, g.bias, g.C = A.data_ptr(), W.data_ptr(), b.data_ptr(), C.data_ptr()
+            g.a_rows_per_batch, g.lda, g.ldw = M, K, K
+            g.c_rows_per_batch, g.ldc = M, N
+            g.M, g.N, g.K, g.epilogue = M, N, K, epi
+            for _ in range(3):
+                wenc.wenc_k_gemm(g)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                wenc.wenc_k_gemm(g)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / steps * 1e3
+            pts.append({"K": K, "us_per_launch": round(us, 2), "us_per_round": round(us / rounds, 3)})
+        x = np.array([p["K"] // 64 for p in pts[2:]], float)
+        y = np.array([p["us_per_round"] for p in pts[2:]])
+        step_us, fixed_us = np.polyfit(x, y, 1)
+        return {"points": pts, "us_per_k_step": round(float(step_us), 3), "us_fixed_per_tile": round(float(fixed_us), 2)}
+
     try:
-        for epi, name in ((wenc.WENC_EPI_GELU_F16, "gelu_f16"), (wenc.WENC_EPI_RESID, "residual_f32")):
-            pts = []
-            for K in (64, 128, 256, 512, 1024, 2048):
-                A = torch.randn(M, K, device="cuda:0").half()
-                W = (0.02 * torch.randn(N, K, device="cuda:0")).half()
-                b = torch.zeros(N, device="cuda:0")
-                C = (torch.empty(M, N, device="cuda:0", dtype=torch.half) if epi == wenc.WENC_EPI_GELU_F16
-                     else torch.zeros(M, N, device="cuda:0"))
-                g = wenc.wenc_gemm_args()
-                g.A, g.W, g.bias, g.C = A.data_ptr(), W.data_ptr(), b.data_ptr(), C.data_ptr()
-                g.a_rows_per_batch, g.lda, g.ldw = M, K, K
-                g.c_rows_per_batch, g.ldc = M, N
-                g.M, g.N, g.K, g.epilogue = M, N, K, epi
-                for _ in range(3):
-                    wenc.wenc_k_gemm(g)
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for _ in range(steps):
-                    wenc.wenc_k_gemm(g)
-                e1.record()
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) / steps * 1e3
-                pts.append({"K": K, "us_per_launch": round(us, 2), "us_per_round": round(us / rounds, 3)})
-            x = np.array([p["K"] // 64 for p in pts[2:]], float)
-            y = np.array([p["us_per_round"] for p in pts[2:]])
-            step_us, fixed_us = np.polyfit(x, y, 1)
-            out[name] = {"points": pts, "us_per_k_step": round(float(step_us), 3), "us_fixed_per_tile": round(float(fixed_us), 2)}
+        for M, N, sfx in ((16384, 4096, ""), (1024, 2048, "_32_tiles")):
+            tiles = M // 256 * (N // 256)
+            rounds = max(1.0, tiles / 256)
+            out["shape" + sfx] = {"M": M, "N": N, "tiles": tiles, "rounds_on_256_cus": rounds}
+            out["gelu_f16" + sfx] = series(M, N, wenc.WENC_EPI_GELU_F16, rounds)
+            out["residual_f32" + sfx] = series(M, N, wenc.WENC_EPI_RESID, rounds)
     finally:
         wenc.lib().wenc_k_gemm_mode(-1, 1)
     print(json.dumps(out), flush=True)

@@ -32,3 +32,29 @@ def test_fair_share_splits_overlaps_evenly():
     assert (share["x"], share["y"], busy) == (5, 5, 10)
     share, busy = ts.fair_share_ns([(0, 12, "x"), (2, 4, "y"), (3, 8, "z")])
     assert sum(share.values()) == pytest.approx(busy) == 12
+
+
+def test_util_by_grid_recovers_the_clock(tmp_path):
+    """GEMM dispatches of two grid sizes: GRBM_GUI_ACTIVE (summed over 8
+    XCDs) = 8 (2.0 GHz x duration + 5000 cycles); the slope over the longest
+    third gives the clock, the intercept the cycles outside the dispatch."""
+    import csv
+    path = tmp_path / "c.csv"
+    name = "void wk::(anonymous namespace)::gemm_kernel<256, 256, 128, 64, 8, 0, 0, 1>(wk::(anonymous namespace)::GemmP)"
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Grid_Size", "Workgroup_Size", "Kernel_Name", "Counter_Name", "Counter_Value",
+                    "Start_Timestamp", "End_Timestamp"])
+        did = 0
+        for wgs, clk in ((1024, 2.0), (32, 2.4)):
+            for dur in (10000, 20000, 40000, 80000, 160000, 320000):
+                did += 1
+                cyc = 8 * (clk * dur + 5000)
+                busy = 1024 * 0.5 * clk * dur
+                w.writerow([did, wgs * 512, 512, name, "GRBM_GUI_ACTIVE", cyc, 0, dur])
+                w.writerow([did, wgs * 512, 512, name, "SQ_VALU_MFMA_BUSY_CYCLES", busy, 0, dur])
+    table = ts.utilisation_by_grid(str(path))
+    rows = [r.split("|")[1:-1] for r in table.splitlines()[2:]]
+    got = {int(r[2]): (float(r[5]), r[6].strip(), r[7].strip()) for r in rows}
+    assert got[1024][0] == pytest.approx(2.0, abs=0.005) and got[32][0] == pytest.approx(2.4, abs=0.005)
+    assert got[1024][1] == "5.0 k" and got[1024][2] == "50.0%"

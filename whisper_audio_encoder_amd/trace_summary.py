@@ -175,6 +175,47 @@ def utilisation(path: str, simds: int = 1024, xcds: int = 8) -> str:
     return "\n".join(out)
 
 
+EPI_NAMES = {0: "GELU fp16", 1: "GELU + positions fp32", 2: "residual fp32", 3: "q|k|v", 4: "cross K/V"}
+
+
+def utilisation_by_grid(path: str, simds: int = 1024, xcds: int = 8) -> str:
+    """GEMM dispatches grouped by epilogue, tile size and workgroup count
+    (bench.py --gemm-tile-costs launches the same kernel over 1024 tiles and
+    over 32 over a range of K).  GRBM_GUI_ACTIVE counts some cycles around
+    each dispatch as well, so the clock is the slope of a least-squares line
+    of cycles against duration over the longest third of a group's
+    dispatches (its largest K), and the MFMA busy share is taken over the
+    cycles of those dispatches at that clock."""
+    with open(path) as fh:
+        rows = list(csv.DictReader(fh))
+    disp = {}
+    for row in rows:
+        d = disp.setdefault(row["Dispatch_Id"], [row["Kernel_Name"], int(row["Grid_Size"]) // int(row["Workgroup_Size"]),
+                                                 int(row["End_Timestamp"]) - int(row["Start_Timestamp"]), {}])
+        d[3][row["Counter_Name"]] = d[3].get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    groups = defaultdict(list)
+    for name, wgs, dur, c in disp.values():
+        m = re.search(r"gemm_kernel<\s*(\d+),\s*(\d+),\s*\d+,\s*\d+,\s*\d+,\s*(\d+),", name)
+        if m:
+            groups[(EPI_NAMES.get(int(m.group(3)), m.group(3)), f"{m.group(1)}x{m.group(2)}", wgs)].append(
+                (dur, c.get("GRBM_GUI_ACTIVE", 0.0) / xcds, c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)))
+    out = ["| epilogue | tile | workgroups | dispatches fitted | their avg us | clock GHz (slope) | "
+           "cycles outside the dispatch | MFMA busy at that clock |",
+           "|---|---|---|---|---|---|---|---|"]
+    for (epi, tile, wgs), rs in sorted(groups.items(), key=lambda kv: (kv[0][0], kv[0][1], -kv[0][2])):
+        rs.sort()
+        top = rs[len(rs) - max(2, len(rs) // 3):]
+        n = len(top)
+        mx = sum(r[0] for r in top) / n
+        my = sum(r[1] for r in top) / n
+        sxx = sum((r[0] - mx) ** 2 for r in top)
+        f = sum((r[0] - mx) * (r[1] - my) for r in top) / sxx if sxx else 0.0  # cycles per ns = GHz
+        extra = my - f * mx
+        busy = sum(r[2] for r in top) / n / (simds * f * mx) if f else 0.0
+        out.append(f"| {epi} | {tile} | {wgs} | {n} | {mx / 1e3:.1f} | {f:.2f} | {extra / 1e3:.1f} k | {100.0 * busy:.1f}% |")
+    return "\n".join(out)
+
+
 def traffic(fetch: str, write: str, copy_fetch: str, copy_write: str, copy_bytes: int, workload: str):
     """HBM bytes per application of each site from FETCH_SIZE and WRITE_SIZE
     (KiB per dispatch), each scaled by what the counter reads for a plain
@@ -221,12 +262,16 @@ def main(argv=None):
     ap.add_argument("--region", default="all", choices=["all", "first", "second"],
                     help="kernel trace of bench.py: its first handle (the timed forward) or its second (one stream)")
     ap.add_argument("--util", action="store_true", help="the file holds GRBM_GUI_ACTIVE and MFMA-busy counters")
+    ap.add_argument("--util-by-grid", action="store_true",
+                    help="as --util, GEMM dispatches grouped by epilogue, tile size and workgroup count")
     ap.add_argument("--traffic", nargs=3, metavar=("WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="the file holds FETCH_SIZE; with the WRITE_SIZE run and the copy calibration runs")
     ap.add_argument("--copy-bytes", type=int, default=268435456)
     ap.add_argument("--json-site", default=None, help="with --traffic: print the JSON record bench.py reads for this site")
     a = ap.parse_args(argv)
-    if a.util:
+    if a.util_by_grid:
+        print(utilisation_by_grid(a.trace))
+    elif a.util:
         print(utilisation(a.trace))
     elif a.traffic:
         md, per_app = traffic(a.trace, *a.traffic, a.copy_bytes, a.workload)
