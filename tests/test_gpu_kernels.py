@@ -247,14 +247,15 @@ def test_gemm_tile_configs_bitwise(epi):
         np.testing.assert_allclose(outs[0][rows].astype(np.float64), oracle.gelu(pre), rtol=1e-3, atol=1e-4)
 
 
-@pytest.mark.parametrize("K", [64, 128, 192, 256, 320, 384, 448, 704, 776])
+@pytest.mark.parametrize("K", [8, 40, 64, 128, 136, 192, 256, 320, 384, 448, 704, 776])
 def test_gemm_every_pipeline_depth(K):
     """The operand pipelines (three LDS buffers for A and two for W, the
     loops unrolled by six; the 128 x 128 and lockstep 256 x 256 loops fetch A
     three k-steps ahead and W two, the ping-pong 256 x 256 loop A two and W
-    one) for 1, 2, 3, 4, 5, 6, 7 and 11 k-steps and 13 with a ragged K tail
-    (776 = 12 x 64 + 8), so each loop leaves at each of its six positions:
-    the fp64 sums within fp32 accumulation, and all three the same bits."""
+    one) for 1, 2, 3, 4, 5, 6, 7 and 11 k-steps, with ragged K tails at 1
+    step (K = 8, 40: the only step is the tail), 3 (136) and 13 (776 = 12 x
+    64 + 8), so each loop leaves at each of its six positions: the fp64 sums
+    within fp32 accumulation, and all three the same bits."""
     M, N = 600, 640
     say(f"gemm pipeline depth K={K}")
     rng = np.random.default_rng(K)
