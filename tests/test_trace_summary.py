@@ -58,3 +58,21 @@ def test_util_by_grid_recovers_the_clock(tmp_path):
     got = {int(r[2]): (float(r[5]), r[6].strip(), r[7].strip()) for r in rows}
     assert got[1024][0] == pytest.approx(2.0, abs=0.005) and got[32][0] == pytest.approx(2.4, abs=0.005)
     assert got[1024][1] == "5.0 k" and got[1024][2] == "50.0%"
+
+
+def test_stalls_per_wave_and_shares(tmp_path):
+    """Two attention dispatches of 100 waves: instructions per wave and the
+    waiting and VALU-active shares of the waves' resident cycles."""
+    import csv
+    path = tmp_path / "s.csv"
+    name = "_ZN2wk12_GLOBAL__N_111attn_kernelEPKDF16_S2_S2_PDF16_iii"
+    vals = {"SQ_WAVES": 100, "SQ_WAVE_CYCLES": 10000, "SQ_WAIT_INST_ANY": 4000, "SQ_ACTIVE_INST_VALU": 2000,
+            "SQ_INSTS_VALU": 12400, "SQ_INSTS_MFMA": 1700, "SQ_INSTS_LDS": 1600}
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"])
+        for did in (1, 2):
+            for k, v in vals.items():
+                w.writerow([did, name, k, v, 0, 5000])
+    row = ts.stalls(str(path)).splitlines()[2].split("|")[1:-1]
+    assert [c.strip() for c in row] == ["attn", "2", "5.0", "100", "124", "17", "16", "40%", "20%"]

@@ -175,6 +175,32 @@ def utilisation(path: str, simds: int = 1024, xcds: int = 8) -> str:
     return "\n".join(out)
 
 
+def stalls(path: str) -> str:
+    """Per kernel of the encoder: instructions per wave (VALU, of which MFMA;
+    LDS) from SQ_INSTS_*, and the share of the waves' resident cycles spent
+    waiting for an instruction's dependencies (SQ_WAIT_INST_ANY /
+    SQ_WAVE_CYCLES) or issuing VALU work (SQ_ACTIVE_INST_VALU /
+    SQ_WAVE_CYCLES).  Counters as rocprofv3 sums them over the device."""
+    groups = defaultdict(list)
+    for name, dur, c in read_counters(path).values():
+        if site_of(name):
+            groups[_kernel_label(name)].append((dur, c))
+    out = ["| kernel (site) | dispatches | avg us | waves | VALU insts per wave | MFMA per wave | LDS insts per wave | "
+           "waiting on dependencies | VALU active |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for label, rows in sorted(groups.items(), key=lambda kv: -sum(r[0] for r in kv[1])):
+        def tot(k):
+            return sum(r[1].get(k, 0.0) for r in rows)
+        waves = tot("SQ_WAVES")
+        wc = tot("SQ_WAVE_CYCLES")
+        per = (lambda k: tot(k) / waves) if waves else (lambda k: 0.0)
+        out.append(f"| {label} | {len(rows)} | {sum(r[0] for r in rows) / len(rows) / 1e3:.1f} | {waves / len(rows):.0f} | "
+                   f"{per('SQ_INSTS_VALU'):.0f} | {per('SQ_INSTS_MFMA'):.0f} | {per('SQ_INSTS_LDS'):.0f} | "
+                   f"{100.0 * tot('SQ_WAIT_INST_ANY') / wc if wc else 0.0:.0f}% | "
+                   f"{100.0 * tot('SQ_ACTIVE_INST_VALU') / wc if wc else 0.0:.0f}% |")
+    return "\n".join(out)
+
+
 EPI_NAMES = {0: "GELU fp16", 1: "GELU + positions fp32", 2: "residual fp32", 3: "q|k|v", 4: "cross K/V"}
 
 
@@ -262,6 +288,8 @@ def main(argv=None):
     ap.add_argument("--region", default="all", choices=["all", "first", "second"],
                     help="kernel trace of bench.py: its first handle (the timed forward) or its second (one stream)")
     ap.add_argument("--util", action="store_true", help="the file holds GRBM_GUI_ACTIVE and MFMA-busy counters")
+    ap.add_argument("--stalls", action="store_true",
+                    help="the file holds SQ_WAVES, SQ_WAVE_CYCLES, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_VALU and SQ_INSTS_*")
     ap.add_argument("--util-by-grid", action="store_true",
                     help="as --util, GEMM dispatches grouped by epilogue, tile size and workgroup count")
     ap.add_argument("--traffic", nargs=3, metavar=("WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -269,7 +297,9 @@ def main(argv=None):
     ap.add_argument("--copy-bytes", type=int, default=268435456)
     ap.add_argument("--json-site", default=None, help="with --traffic: print the JSON record bench.py reads for this site")
     a = ap.parse_args(argv)
-    if a.util_by_grid:
+    if a.stalls:
+        print(stalls(a.trace))
+    elif a.util_by_grid:
         print(utilisation_by_grid(a.trace))
     elif a.util:
         print(utilisation(a.trace))
