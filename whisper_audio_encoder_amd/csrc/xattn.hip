@@ -28,8 +28,13 @@ namespace wk {
 
 namespace {
 
-constexpr int XNW = 4;          // waves per workgroup of pass 1
-constexpr int XKC = 64 * XNW;  // keys per workgroup of pass 1
+// Waves per workgroup of pass 1 (each takes 64 keys) for NQ query rows.
+// Measured at 16 windows x 1500 keys x 20 heads: 8 waves against 4 is 5%
+// faster per layer for one query and 9% for four, and 7% slower for eight,
+// whose larger per-lane state makes the wider workgroup's waves wait longer.
+constexpr int xnw(int nq) { return nq <= 4 ? 8 : 4; }
+constexpr int xkc(int nq) { return 64 * xnw(nq); }  // keys per workgroup of pass 1
+constexpr int XNW_MIN = 4;  // the fewest keys per workgroup over every NQ: 64 XNW_MIN
 constexpr int XPART = 68;  // floats per partial: max, sum, o[64], 2 pad (16-byte rows)
 constexpr float LOG2E_8 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
 
@@ -45,7 +50,7 @@ __device__ __forceinline__ float wave_add(float v) {
     return v;
 }
 
-template <int NQ>
+template <int NQ, int XNW = xnw(NQ)>
 __global__ void __launch_bounds__(64 * XNW)
 xattn_partial(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *__restrict__ xv,
               float *__restrict__ part, int T, int H, int nc) {
@@ -71,7 +76,7 @@ xattn_partial(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *
     // so one instruction covers 8 whole 128-byte rows.  The loads are buffer
     // loads over this window's K and V (a key at or past T has an offset past
     // the range and reads zero), all issued before the scores, K first.
-    const int key0 = c * XKC + wave * 64;
+    const int key0 = c * (64 * XNW) + wave * 64;
     const int dq = lane & 7, r8 = lane >> 3;
     const uint32_t range = uint32_t(T) * uint32_t(d) * 2u;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -210,8 +215,8 @@ xattn_merge(const float *__restrict__ part, f16 *__restrict__ out, int H, int nc
 template <int NQ>
 hipError_t xattn_dispatch(const f16 *q, const f16 *xk, const f16 *xv, f16 *out, float *part, int B, int H, int T,
                           hipStream_t s) {
-    const int nc = (T + XKC - 1) / XKC;
-    xattn_partial<NQ><<<dim3(unsigned(B * H * nc)), dim3(64 * XNW), 0, s>>>(q, xk, xv, part, T, H, nc);
+    const int nc = (T + xkc(NQ) - 1) / xkc(NQ);
+    xattn_partial<NQ><<<dim3(unsigned(B * H * nc)), dim3(64 * xnw(NQ)), 0, s>>>(q, xk, xv, part, T, H, nc);
     xattn_merge<NQ><<<dim3(unsigned(B * H)), dim3(64), 0, s>>>(part, out, H, nc);
     return hipGetLastError();
 }
@@ -219,7 +224,7 @@ hipError_t xattn_dispatch(const f16 *q, const f16 *xk, const f16 *xv, f16 *out, 
 }  // namespace
 
 size_t xattn_part_bytes(int batch, int n_head, int n_q, int T) {
-    const size_t nc = size_t(T + XKC - 1) / XKC;
+    const size_t nc = size_t(T + xkc(n_q) - 1) / xkc(n_q);
     return size_t(batch) * n_head * nc * n_q * XPART * sizeof(float);
 }
 
@@ -228,7 +233,8 @@ const char *xattn_check(int batch, int n_head, int n_q, int T) {
     if (n_q < 1 || n_q > XATTN_MAX_Q) return "cross attention: n_q must be in [1, 8]";
     if (T < 1) return "cross attention: n_ctx must be >= 1";
     if (int64_t(T) * n_head * 64 * 2 >= (int64_t(1) << 31)) return "cross attention: a window's K or V exceeds 2 GiB";
-    if (int64_t(batch) * n_head * ((T + XKC - 1) / XKC) >= (int64_t(1) << 31)) return "cross attention: grid too large";
+    if (int64_t(batch) * n_head * ((T + 64 * XNW_MIN - 1) / (64 * XNW_MIN)) >= (int64_t(1) << 31))
+        return "cross attention: grid too large";
     return nullptr;
 }
 
