@@ -30,8 +30,10 @@ namespace {
 
 // Waves per workgroup of pass 1 (each takes 64 keys) for NQ query rows.
 // Measured at 16 windows x 1500 keys x 20 heads: 8 waves against 4 is 5%
-// faster per layer for one query and 9% for four, and 7% slower for eight,
-// whose larger per-lane state makes the wider workgroup's waves wait longer.
+// faster per layer (both passes) for one query and 9% for four, and 7% slower
+// for eight, whose larger per-lane state makes the wider workgroup's waves
+// wait longer.  The saving is the merge's, which reads half as many partials;
+// pass 1 alone is a few percent slower with 8 waves.
 constexpr int xnw(int nq) { return nq <= 4 ? 8 : 4; }
 constexpr int xkc(int nq) { return 64 * xnw(nq); }  // keys per workgroup of pass 1
 constexpr int XNW_MIN = 4;  // the fewest keys per workgroup over every NQ: 64 XNW_MIN
