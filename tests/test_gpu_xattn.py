@@ -47,10 +47,19 @@ def _run(enc, q, xk, xv):
     return host(out).astype(np.float64)
 
 
-# (config whose handle is used, B, n_q, T): one query at the full 1500 keys; a
-# few queries; ragged key counts (one key, 257 = one chunk + 1, 777); beams of 8
+# (config whose handle is used, B, n_q, T).  The first ten take the two-pass
+# path (few (b, h) pairs): one query at the full 1500 keys; a few queries;
+# beams of 8; ragged key counts against the keys a workgroup of the first
+# pass takes (512 for up to 4 query rows, 256 for more): one key, 64, 257,
+# 513 (one workgroup + 1), 777, 1024 (exactly two) and 257 with 6 rows.  The
+# next four take the one-pass path on a 256-CU MI355X (up to 4 rows and
+# B x n_head pairs of 0.7 to 1.0 per CU): full, ragged and single keys (T = 1
+# leaves every wave but the first without a tile).  The last three are large
+# batches of 5 to 8 rows, which keep the two passes.
 CASES = [("c4", 2, 1, 1500), ("c4", 3, 3, 777), ("c3", 2, 8, 1500), ("c3", 4, 2, 257), ("c1", 1, 1, 1),
-         ("c1", 5, 4, 64), ("c2", 8, 1, 1500)]
+         ("c1", 5, 4, 64), ("c2", 8, 1, 1500), ("c3", 3, 2, 513), ("c2", 2, 4, 1024), ("c1", 3, 6, 257),
+         ("c4", 12, 1, 1500), ("c3", 16, 3, 777), ("c2", 24, 2, 513), ("c1", 40, 4, 1),
+         ("c4", 8, 8, 1500), ("c2", 40, 6, 65), ("c1", 30, 5, 777)]
 
 
 @pytest.mark.parametrize("name,B,n_q,T", CASES)
@@ -113,6 +122,27 @@ def test_cross_attend_deterministic_and_chunked():
         assert np.array_equal(one[0], a[i])
     np.testing.assert_allclose(a[[0, 39]].astype(np.float64), _oracle(q[[0, 39]], xk[[0, 39]], xv[[0, 39]], H),
                                rtol=1e-3, atol=1e-4)
+
+
+@pytest.mark.parametrize("name,B,n_q,T", [("c4", 12, 1, 1500), ("c3", 16, 4, 700), ("c2", 30, 3, 1500),
+                                           ("c1", 40, 2, 1)])
+def test_cross_attend_one_pass_matches_two_passes_bitwise(name, B, n_q, T):
+    """A batch whose (b, h) pairs about fill a 256-CU MI355X once runs the
+    one-pass kernel; each of its items alone runs the two launches.  The one
+    pass repeats the two passes' arithmetic in their order, so every output
+    bit agrees: the result does not depend on the batch it was computed in."""
+    H = inputs(name)[0].n_head
+    say(f"cross attend one pass vs two {name} B={B} n_q={n_q} T={T}")
+    rng = np.random.default_rng(B * 31 + n_q * 7 + T)
+    q, xk, xv = _case(rng, B, H, n_q, T, q_scale=4.0)
+    enc = encoder(name)
+    qd, kd, vd = f16_dev(q), f16_dev(xk), f16_dev(xv)
+    a = host(enc.cross_attend(qd, kd, vd))
+    for i in sorted({0, B // 2, B - 1}):
+        one = host(enc.cross_attend(qd[i:i + 1].contiguous(), kd[i:i + 1].contiguous(), vd[i:i + 1].contiguous()))
+        assert np.array_equal(one[0].view(np.uint16), a[i].view(np.uint16)), f"item {i}"
+    np.testing.assert_allclose(a[[0, B - 1]].astype(np.float64), _oracle(q[[0, B - 1]], xk[[0, B - 1]],
+                               xv[[0, B - 1]], H), rtol=1e-3, atol=1e-4)
 
 
 def test_cross_attend_error_paths():

@@ -11,6 +11,7 @@
 // describes the remedy its one-query kernel uses: split the keys across
 // workgroups and merge the partial softmaxes.  The layout below is our own.
 //
+// Two passes (the default) or one, chosen per launch (xattn_one_pass).
 // Pass 1 (xattn_partial): a workgroup takes 64 keys per wave of one (b, h);
 // K and V rows are read 8 lanes to a row (16 bytes a lane), the partial dot
 // products of a key's 8 lanes (fp16 pairs accumulated in fp32) are summed by
@@ -20,7 +21,9 @@
 // o[64]) per query.  Pass 2
 // (xattn_merge): one wave per (b, h) rescales the partials to a common
 // maximum and sums them in key order, so the result does not depend on
-// scheduling.  The work is bound by reading K and V once (HBM).
+// scheduling.  One pass (xattn_whole): a workgroup per (b, h) walks all its
+// keys, 64 per wave at a time, with an online softmax, and writes out.  The
+// work is bound by reading K and V once (HBM).
 #include "common.h"
 #include "kernels.h"
 
@@ -52,40 +55,20 @@ __device__ __forceinline__ float wave_add(float v) {
     return v;
 }
 
-template <int NQ, int XNW = xnw(NQ)>
-__global__ void __launch_bounds__(64 * XNW)
-xattn_partial(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *__restrict__ xv,
-              float *__restrict__ part, int T, int H, int nc) {
-    const int wg = blockIdx.x;
-    const int c = wg % nc, bh = wg / nc;
-    const int h = bh % H, b = bh / H;
-    const int64_t d = int64_t(H) * 64;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Buffer descriptor over one window's K or V rows: offsets at or past the
+// window's T rows read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t xrsrc(const f16 *x, int b, int T, int64_t d) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<f16 *>(x) + int64_t(b) * T * d, 0,
+                                             int(uint32_t(T) * uint32_t(d) * 2u), 0x00020000);
+}
 
-    __shared__ f16x2 qs[NQ][32];      // the queries of (b, h), fp16 pairs
-    __shared__ float ps[XNW][NQ][64];  // probabilities, by wave and key
-    __shared__ float wm[XNW][NQ], wl[XNW][NQ];
-    __shared__ float wo[XNW][NQ][64];
-
-    for (int i = tid; i < NQ * 32; i += 64 * XNW) {
-        const int qi = i / 32, e2 = i % 32;
-        qs[qi][e2] = *reinterpret_cast<const f16x2 *>(q + (int64_t(b) * NQ + qi) * d + h * 64 + 2 * e2);
-    }
-    __syncthreads();
-
-    // K and V rows are both read 8 lanes to a row: in load it, lane (r8 =
-    // lane >> 3, dq = lane & 7) holds dimensions 8 dq .. +7 of key 8 it + r8,
-    // so one instruction covers 8 whole 128-byte rows.  The loads are buffer
-    // loads over this window's K and V (a key at or past T has an offset past
-    // the range and reads zero), all issued before the scores, K first.
-    const int key0 = c * (64 * XNW) + wave * 64;
-    const int dq = lane & 7, r8 = lane >> 3;
-    const uint32_t range = uint32_t(T) * uint32_t(d) * 2u;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<f16 *>(xk) + int64_t(b) * T * d, 0, int(range), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<f16 *>(xv) + int64_t(b) * T * d, 0, int(range), 0x00020000);
-    f16x8 kv[8], vv[8];
+// K and V rows are both read 8 lanes to a row: in load it, lane (r8 = lane
+// >> 3, dq = lane & 7) holds dimensions 8 dq .. +7 of key key0 + 8 it + r8,
+// so one instruction covers 8 whole 128-byte rows.  Buffer loads: a key at
+// or past T has an offset past the range and reads zero.  All are issued
+// before the scores, K first.
+__device__ __forceinline__ void xload(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int key0, int T,
+                                      int64_t d, int h, int dq, int r8, f16x8 (&kv)[8], f16x8 (&vv)[8]) {
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
         const int uu = key0 + 8 * it + r8;
@@ -98,12 +81,16 @@ xattn_partial(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *
         const uint32_t off = uu < T ? uint32_t((int64_t(uu) * d + h * 64 + 8 * dq) * 2) : 0x80000000u;
         vv[it] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
-    // scores (base 2, scaled by log2(e)/8): each lane's partial dot product
-    // over its 8 dimensions, then a reduce-scatter over the 8 lanes of a row
-    // (exchanging 4, 2, 1 partials with lanes dq ^ 4, ^ 2, ^ 1), after which
-    // lane (r8, dq) holds the whole score of key u = 8 dq + r8.
-    const int u = key0 + 8 * dq + r8;
-    float s[NQ];
+}
+
+// Scores (base 2, scaled by log2(e)/8) of the loaded keys: each lane's
+// partial dot product over its 8 dimensions, then a reduce-scatter over the
+// 8 lanes of a row (exchanging 4, 2, 1 partials with lanes dq ^ 4, ^ 2, ^ 1),
+// after which lane (r8, dq) holds the whole score of key u = key0 + 8 dq +
+// r8 (-inf for u >= T).
+template <int NQ>
+__device__ __forceinline__ void xscores(const f16x8 (&kv)[8], const f16x2 (&qs)[NQ][32], int u, int T, int dq,
+                                        float (&s)[NQ]) {
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
         float v8[8];
@@ -124,33 +111,27 @@ xattn_partial(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *
         const float full = (b1 ? v2[1] : v2[0]) + __shfl_xor(b1 ? v2[0] : v2[1], 1);
         s[i] = u < T ? full * LOG2E_8 : -INFINITY;
     }
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-        const float m = wave_max(s[i]);  // -inf only when every key of the wave is past T
-        const float p = u < T ? __builtin_amdgcn_exp2f(s[i] - m) : 0.f;
-        const float l = wave_add(p);
-        ps[wave][i][8 * dq + r8] = p;
-        if (lane == 0) {
-            wm[wave][i] = m;
-            wl[wave][i] = l;
-        }
-    }
-    // ps is written and read by the same wave: LDS operations of a wave
-    // complete in order.  P.V over the wave's rows, then a sum over the 8
-    // lanes that share a dimension group (lane bits 3..5).
-    float oa[NQ][8];
-#pragma unroll
-    for (int i = 0; i < NQ; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) oa[i][e] = 0.f;
+}
+
+// oa += P.V over the loaded rows: lane (r8, dq) takes the probabilities of
+// keys 8 it + r8 from the wave's LDS row ps (written by the same wave: LDS
+// operations of a wave complete in order) against its 8 dimensions of them.
+template <int NQ>
+__device__ __forceinline__ void xpv(const f16x8 (&vv)[8], const float (&ps)[NQ][64], int r8, float (&oa)[NQ][8]) {
 #pragma unroll
     for (int it = 0; it < 8; ++it)
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
-            const float p = ps[wave][i][8 * it + r8];
+            const float p = ps[i][8 * it + r8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) oa[i][e] = fmaf(p, float(vv[it][e]), oa[i][e]);
         }
+}
+
+// Sum over the 8 lanes that share a dimension group (lane bits 3..5); lanes
+// with r8 == 0 then write the wave's o[64] per query.
+template <int NQ>
+__device__ __forceinline__ void xreduce_store(float (&oa)[NQ][8], float (&wo)[NQ][64], int r8, int dq) {
 #pragma unroll
     for (int i = 0; i < NQ; ++i)
 #pragma unroll
@@ -163,8 +144,62 @@ xattn_partial(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *
 #pragma unroll
         for (int i = 0; i < NQ; ++i)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) wo[wave][i][8 * dq + e] = oa[i][e];
+            for (int e = 0; e < 8; ++e) wo[i][8 * dq + e] = oa[i][e];
     }
+}
+
+// The queries of (b, h) as fp16 pairs in LDS.
+template <int NQ, int NT>
+__device__ __forceinline__ void xload_q(const f16 *q, f16x2 (&qs)[NQ][32], int b, int h, int64_t d, int tid) {
+    for (int i = tid; i < NQ * 32; i += NT) {
+        const int qi = i / 32, e2 = i % 32;
+        qs[qi][e2] = *reinterpret_cast<const f16x2 *>(q + (int64_t(b) * NQ + qi) * d + h * 64 + 2 * e2);
+    }
+}
+
+template <int NQ, int XNW = xnw(NQ)>
+__global__ void __launch_bounds__(64 * XNW)
+xattn_partial(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *__restrict__ xv,
+              float *__restrict__ part, int T, int H, int nc) {
+    const int wg = blockIdx.x;
+    const int c = wg % nc, bh = wg / nc;
+    const int h = bh % H, b = bh / H;
+    const int64_t d = int64_t(H) * 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    __shared__ f16x2 qs[NQ][32];      // the queries of (b, h), fp16 pairs
+    __shared__ float ps[XNW][NQ][64];  // probabilities, by wave and key
+    __shared__ float wm[XNW][NQ], wl[XNW][NQ];
+    __shared__ float wo[XNW][NQ][64];
+
+    xload_q<NQ, 64 * XNW>(q, qs, b, h, d, tid);
+    __syncthreads();
+
+    const int key0 = c * (64 * XNW) + wave * 64;
+    const int dq = lane & 7, r8 = lane >> 3;
+    f16x8 kv[8], vv[8];
+    xload(xrsrc(xk, b, T, d), xrsrc(xv, b, T, d), key0, T, d, h, dq, r8, kv, vv);
+    const int u = key0 + 8 * dq + r8;
+    float s[NQ];
+    xscores<NQ>(kv, qs, u, T, dq, s);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const float m = wave_max(s[i]);  // -inf only when every key of the wave is past T
+        const float p = u < T ? __builtin_amdgcn_exp2f(s[i] - m) : 0.f;
+        const float l = wave_add(p);
+        ps[wave][i][8 * dq + r8] = p;
+        if (lane == 0) {
+            wm[wave][i] = m;
+            wl[wave][i] = l;
+        }
+    }
+    float oa[NQ][8];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oa[i][e] = 0.f;
+    xpv<NQ>(vv, ps[wave], r8, oa);
+    xreduce_store<NQ>(oa, wo[wave], r8, dq);
     __syncthreads();
 
     // the workgroup's partial per query: its waves at a common maximum
@@ -187,6 +222,97 @@ xattn_partial(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *
             pp[0] = M;
             pp[1] = L;
         }
+    }
+}
+
+// One pass, for batches whose (b, h) pairs about fill the compute units: a
+// workgroup takes every key of one (b, h) and runs both passes' arithmetic
+// in their order, so its output has the same bits as the two launches.  In
+// round c its waves take the 64-key tiles of key chunk c (64 XNW keys) as
+// pass 1 does and merge them into the chunk's (max, sum, o[64]), kept in
+// LDS; after the last round the chunks merge as pass 2 does.  No partials
+// leave the chip and no second launch follows.  nc <= XNC_MAX.
+constexpr int XNC_MAX = 8;
+
+template <int NQ, int XNW = xnw(NQ)>
+__global__ void __launch_bounds__(64 * XNW)
+xattn_whole(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *__restrict__ xv,
+            f16 *__restrict__ out, int T, int H, int nc) {
+    const int bh = blockIdx.x;
+    const int h = bh % H, b = bh / H;
+    const int64_t d = int64_t(H) * 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    __shared__ f16x2 qs[NQ][32];
+    __shared__ float ps[XNW][NQ][64];
+    __shared__ float wm[XNW][NQ], wl[XNW][NQ];
+    __shared__ float wo[XNW][NQ][64];
+    __shared__ float cm[XNC_MAX][NQ], cl[XNC_MAX][NQ];
+    __shared__ float co[XNC_MAX][NQ][64];
+
+    xload_q<NQ, 64 * XNW>(q, qs, b, h, d, tid);
+    __syncthreads();
+
+    const int dq = lane & 7, r8 = lane >> 3;
+    const __amdgpu_buffer_rsrc_t rk = xrsrc(xk, b, T, d), rv = xrsrc(xv, b, T, d);
+    for (int c = 0; c < nc; ++c) {
+        const int key0 = c * (64 * XNW) + wave * 64;
+        f16x8 kv[8], vv[8];
+        xload(rk, rv, key0, T, d, h, dq, r8, kv, vv);
+        const int u = key0 + 8 * dq + r8;
+        float s[NQ];
+        xscores<NQ>(kv, qs, u, T, dq, s);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const float m = wave_max(s[i]);
+            const float p = u < T ? __builtin_amdgcn_exp2f(s[i] - m) : 0.f;
+            const float l = wave_add(p);
+            ps[wave][i][8 * dq + r8] = p;
+            if (lane == 0) {
+                wm[wave][i] = m;
+                wl[wave][i] = l;
+            }
+        }
+        float oa[NQ][8];
+#pragma unroll
+        for (int i = 0; i < NQ; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) oa[i][e] = 0.f;
+        xpv<NQ>(vv, ps[wave], r8, oa);
+        xreduce_store<NQ>(oa, wo[wave], r8, dq);
+        __syncthreads();
+        for (int idx = tid; idx < NQ * 64; idx += 64 * XNW) {
+            const int i = idx / 64, e = idx % 64;
+            float M = wm[0][i];
+#pragma unroll
+            for (int w = 1; w < XNW; ++w) M = fmaxf(M, wm[w][i]);
+            float L = 0.f, O = 0.f;
+#pragma unroll
+            for (int w = 0; w < XNW; ++w) {
+                const float sc = __builtin_amdgcn_exp2f(wm[w][i] - M);
+                L = fmaf(sc, wl[w][i], L);
+                O = fmaf(sc, wo[w][i][e], O);
+            }
+            co[c][i][e] = O;
+            if (e == 0) {
+                cm[c][i] = M;
+                cl[c][i] = L;
+            }
+        }
+        __syncthreads();  // the next round rewrites wm, wl and wo
+    }
+
+    for (int idx = tid; idx < NQ * 64; idx += 64 * XNW) {
+        const int i = idx / 64, e = idx % 64;
+        float M = cm[0][i];
+        for (int c = 1; c < nc; ++c) M = fmaxf(M, cm[c][i]);
+        float L = 0.f, O = 0.f;
+        for (int c = 0; c < nc; ++c) {
+            const float sc = __builtin_amdgcn_exp2f(cm[c][i] - M);
+            L = fmaf(sc, cl[c][i], L);
+            O = fmaf(sc, co[c][i][e], O);
+        }
+        out[(int64_t(b) * NQ + i) * d + h * 64 + e] = f16(O / L);
     }
 }
 
@@ -214,10 +340,28 @@ xattn_merge(const float *__restrict__ part, f16 *__restrict__ out, int H, int nc
     }
 }
 
+// One pass or two.  The one pass takes a (b, h) in rounds, one key chunk
+// each, so it pays when the pairs nearly fill the compute units once: with
+// fewer, too few units pull from memory; with more, some units hold two
+// workgroups and finish last, while the two-pass split balances them.
+// Measured per layer at 1500 keys over 80 to 320 pairs on 256 units (4, 8,
+// 12, 16 windows x 20 heads; 16 x 12): up to 4 query rows the one pass wins
+// at 0.75 and 0.94 pairs per unit (-5% to -8%) and loses at 0.31, 0.63 and
+// 1.25.  With 5 to 8 rows (256-key chunks, six rounds of two barriers each)
+// it loses everywhere.  The bits are the same either way.
+bool xattn_one_pass(int64_t pairs, int nq, long cus) {
+    const double r = double(pairs) / double(cus);
+    return nq <= 4 && r >= 0.7 && r <= 1.0;
+}
+
 template <int NQ>
 hipError_t xattn_dispatch(const f16 *q, const f16 *xk, const f16 *xv, f16 *out, float *part, int B, int H, int T,
                           hipStream_t s) {
     const int nc = (T + xkc(NQ) - 1) / xkc(NQ);
+    if (nc <= XNC_MAX && xattn_one_pass(int64_t(B) * H, NQ, cu_count())) {
+        xattn_whole<NQ><<<dim3(unsigned(B * H)), dim3(64 * xnw(NQ)), 0, s>>>(q, xk, xv, out, T, H, nc);
+        return hipGetLastError();
+    }
     xattn_partial<NQ><<<dim3(unsigned(B * H * nc)), dim3(64 * xnw(NQ)), 0, s>>>(q, xk, xv, part, T, H, nc);
     xattn_merge<NQ><<<dim3(unsigned(B * H)), dim3(64), 0, s>>>(part, out, H, nc);
     return hipGetLastError();
