@@ -157,28 +157,18 @@ __device__ __forceinline__ void xload_q(const f16 *q, f16x2 (&qs)[NQ][32], int b
     }
 }
 
-template <int NQ, int XNW = xnw(NQ)>
-__global__ void __launch_bounds__(64 * XNW)
-xattn_partial(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *__restrict__ xv,
-              float *__restrict__ part, int T, int H, int nc) {
-    const int wg = blockIdx.x;
-    const int c = wg % nc, bh = wg / nc;
-    const int h = bh % H, b = bh / H;
-    const int64_t d = int64_t(H) * 64;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    __shared__ f16x2 qs[NQ][32];      // the queries of (b, h), fp16 pairs
-    __shared__ float ps[XNW][NQ][64];  // probabilities, by wave and key
-    __shared__ float wm[XNW][NQ], wl[XNW][NQ];
-    __shared__ float wo[XNW][NQ][64];
-
-    xload_q<NQ, 64 * XNW>(q, qs, b, h, d, tid);
-    __syncthreads();
-
-    const int key0 = c * (64 * XNW) + wave * 64;
+// Pass 1's work for one wave: the 64 keys key0 .. key0 + 63 of (b, h) give
+// the wave's maximum, exp2 sum and o[64] per query, written to its rows of
+// wm, wl and wo (a wave whose keys all lie at or past T has maximum -inf,
+// sum 0 and o 0).
+template <int NQ, int XNW>
+__device__ __forceinline__ void xwave_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int key0, int T,
+                                           int64_t d, int h, int lane, int wave, const f16x2 (&qs)[NQ][32],
+                                           float (&ps)[XNW][NQ][64], float (&wm)[XNW][NQ], float (&wl)[XNW][NQ],
+                                           float (&wo)[XNW][NQ][64]) {
     const int dq = lane & 7, r8 = lane >> 3;
     f16x8 kv[8], vv[8];
-    xload(xrsrc(xk, b, T, d), xrsrc(xv, b, T, d), key0, T, d, h, dq, r8, kv, vv);
+    xload(rk, rv, key0, T, d, h, dq, r8, kv, vv);
     const int u = key0 + 8 * dq + r8;
     float s[NQ];
     xscores<NQ>(kv, qs, u, T, dq, s);
@@ -200,22 +190,69 @@ xattn_partial(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *
         for (int e = 0; e < 8; ++e) oa[i][e] = 0.f;
     xpv<NQ>(vv, ps[wave], r8, oa);
     xreduce_store<NQ>(oa, wo[wave], r8, dq);
+}
+
+// A workgroup's partial for query i, column e: its waves at a common maximum,
+// in wave order (a wave with maximum -inf has weight 0).
+template <int NQ, int XNW>
+__device__ __forceinline__ void xmerge_waves(const float (&wm)[XNW][NQ], const float (&wl)[XNW][NQ],
+                                             const float (&wo)[XNW][NQ][64], int i, int e, float &M, float &L,
+                                             float &O) {
+    M = wm[0][i];
+#pragma unroll
+    for (int w = 1; w < XNW; ++w) M = fmaxf(M, wm[w][i]);
+    L = 0.f;
+    O = 0.f;
+#pragma unroll
+    for (int w = 0; w < XNW; ++w) {
+        const float sc = __builtin_amdgcn_exp2f(wm[w][i] - M);
+        L = fmaf(sc, wl[w][i], L);
+        O = fmaf(sc, wo[w][i][e], O);
+    }
+}
+
+// Pass 2's merge of nc chunk partials (max m(c), sum l(c), column o(c)) in
+// chunk order: the output value sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c.
+template <class Fm, class Fl, class Fo>
+__device__ __forceinline__ float xmerge_chunks(int nc, Fm m, Fl l, Fo o) {
+    float M = m(0);
+    for (int c = 1; c < nc; ++c) M = fmaxf(M, m(c));
+    float L = 0.f, O = 0.f;
+    for (int c = 0; c < nc; ++c) {
+        const float sc = __builtin_amdgcn_exp2f(m(c) - M);
+        L = fmaf(sc, l(c), L);
+        O = fmaf(sc, o(c), O);
+    }
+    return O / L;
+}
+
+template <int NQ, int XNW = xnw(NQ)>
+__global__ void __launch_bounds__(64 * XNW)
+xattn_partial(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *__restrict__ xv,
+              float *__restrict__ part, int T, int H, int nc) {
+    const int wg = blockIdx.x;
+    const int c = wg % nc, bh = wg / nc;
+    const int h = bh % H, b = bh / H;
+    const int64_t d = int64_t(H) * 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    __shared__ f16x2 qs[NQ][32];      // the queries of (b, h), fp16 pairs
+    __shared__ float ps[XNW][NQ][64];  // probabilities, by wave and key
+    __shared__ float wm[XNW][NQ], wl[XNW][NQ];
+    __shared__ float wo[XNW][NQ][64];
+
+    xload_q<NQ, 64 * XNW>(q, qs, b, h, d, tid);
     __syncthreads();
 
-    // the workgroup's partial per query: its waves at a common maximum
-    // (a wave whose keys all lie past T has maximum -inf and weight 0)
+    xwave_tile<NQ, XNW>(xrsrc(xk, b, T, d), xrsrc(xv, b, T, d), c * (64 * XNW) + wave * 64, T, d, h, lane, wave, qs,
+                        ps, wm, wl, wo);
+    __syncthreads();
+
+    // the workgroup's partial per query
     for (int idx = tid; idx < NQ * 64; idx += 64 * XNW) {
         const int i = idx / 64, e = idx % 64;
-        float M = wm[0][i];
-#pragma unroll
-        for (int w = 1; w < XNW; ++w) M = fmaxf(M, wm[w][i]);
-        float L = 0.f, O = 0.f;
-#pragma unroll
-        for (int w = 0; w < XNW; ++w) {
-            const float sc = __builtin_amdgcn_exp2f(wm[w][i] - M);
-            L = fmaf(sc, wl[w][i], L);
-            O = fmaf(sc, wo[w][i][e], O);
-        }
+        float M, L, O;
+        xmerge_waves<NQ, XNW>(wm, wl, wo, i, e, M, L, O);
         float *pp = part + ((int64_t(bh) * nc + c) * NQ + i) * XPART;
         pp[2 + e] = O;
         if (e == 0) {
@@ -253,46 +290,14 @@ xattn_whole(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *__
     xload_q<NQ, 64 * XNW>(q, qs, b, h, d, tid);
     __syncthreads();
 
-    const int dq = lane & 7, r8 = lane >> 3;
     const __amdgpu_buffer_rsrc_t rk = xrsrc(xk, b, T, d), rv = xrsrc(xv, b, T, d);
     for (int c = 0; c < nc; ++c) {
-        const int key0 = c * (64 * XNW) + wave * 64;
-        f16x8 kv[8], vv[8];
-        xload(rk, rv, key0, T, d, h, dq, r8, kv, vv);
-        const int u = key0 + 8 * dq + r8;
-        float s[NQ];
-        xscores<NQ>(kv, qs, u, T, dq, s);
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-            const float m = wave_max(s[i]);
-            const float p = u < T ? __builtin_amdgcn_exp2f(s[i] - m) : 0.f;
-            const float l = wave_add(p);
-            ps[wave][i][8 * dq + r8] = p;
-            if (lane == 0) {
-                wm[wave][i] = m;
-                wl[wave][i] = l;
-            }
-        }
-        float oa[NQ][8];
-#pragma unroll
-        for (int i = 0; i < NQ; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) oa[i][e] = 0.f;
-        xpv<NQ>(vv, ps[wave], r8, oa);
-        xreduce_store<NQ>(oa, wo[wave], r8, dq);
+        xwave_tile<NQ, XNW>(rk, rv, c * (64 * XNW) + wave * 64, T, d, h, lane, wave, qs, ps, wm, wl, wo);
         __syncthreads();
         for (int idx = tid; idx < NQ * 64; idx += 64 * XNW) {
             const int i = idx / 64, e = idx % 64;
-            float M = wm[0][i];
-#pragma unroll
-            for (int w = 1; w < XNW; ++w) M = fmaxf(M, wm[w][i]);
-            float L = 0.f, O = 0.f;
-#pragma unroll
-            for (int w = 0; w < XNW; ++w) {
-                const float sc = __builtin_amdgcn_exp2f(wm[w][i] - M);
-                L = fmaf(sc, wl[w][i], L);
-                O = fmaf(sc, wo[w][i][e], O);
-            }
+            float M, L, O;
+            xmerge_waves<NQ, XNW>(wm, wl, wo, i, e, M, L, O);
             co[c][i][e] = O;
             if (e == 0) {
                 cm[c][i] = M;
@@ -304,15 +309,8 @@ xattn_whole(const f16 *__restrict__ q, const f16 *__restrict__ xk, const f16 *__
 
     for (int idx = tid; idx < NQ * 64; idx += 64 * XNW) {
         const int i = idx / 64, e = idx % 64;
-        float M = cm[0][i];
-        for (int c = 1; c < nc; ++c) M = fmaxf(M, cm[c][i]);
-        float L = 0.f, O = 0.f;
-        for (int c = 0; c < nc; ++c) {
-            const float sc = __builtin_amdgcn_exp2f(cm[c][i] - M);
-            L = fmaf(sc, cl[c][i], L);
-            O = fmaf(sc, co[c][i][e], O);
-        }
-        out[(int64_t(b) * NQ + i) * d + h * 64 + e] = f16(O / L);
+        out[(int64_t(b) * NQ + i) * d + h * 64 + e] = f16(xmerge_chunks(
+            nc, [&](int c) { return cm[c][i]; }, [&](int c) { return cl[c][i]; }, [&](int c) { return co[c][i][e]; }));
     }
 }
 
@@ -327,16 +325,10 @@ xattn_merge(const float *__restrict__ part, f16 *__restrict__ out, int H, int nc
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
         const float *p0 = part + (int64_t(bh) * nc * NQ + i) * XPART;
-        float M = p0[0];
-        for (int c = 1; c < nc; ++c) M = fmaxf(M, p0[int64_t(c) * NQ * XPART]);
-        float L = 0.f, O = 0.f;
-        for (int c = 0; c < nc; ++c) {
-            const float *pc = p0 + int64_t(c) * NQ * XPART;
-            const float sc = __builtin_amdgcn_exp2f(pc[0] - M);
-            L = fmaf(sc, pc[1], L);
-            O = fmaf(sc, pc[2 + e], O);
-        }
-        out[(int64_t(b) * NQ + i) * d + h * 64 + e] = f16(O / L);
+        const int64_t cs = int64_t(NQ) * XPART;  // floats from one chunk's partial to the next
+        out[(int64_t(b) * NQ + i) * d + h * 64 + e] = f16(xmerge_chunks(
+            nc, [&](int c) { return p0[c * cs]; }, [&](int c) { return p0[c * cs + 1]; },
+            [&](int c) { return p0[c * cs + 2 + e]; }));
     }
 }
 
