@@ -284,8 +284,11 @@ int wenc_k_gemm(const wenc_gemm_args *args, void *stream);
  * greedy decoding, a few for beams), 1 <= n_ctx <= cfg.n_ctx, batch >= 0
  * (chunked through the handle's activation scratch, which it shares with
  * wenc_forward: one call at a time per handle).  Scores, probabilities and
- * sums are fp32; out is rounded to fp16 once.  Enqueues on `stream`, no
- * host sync.  EINVAL for bad sizes, NULL or misaligned pointers. */
+ * sums are fp32; out is rounded to fp16 once.  Deterministic, and an item's
+ * output bits do not depend on the batch it is computed in (the library
+ * picks one launch or two by the batch's size; both sum in the same order).
+ * Enqueues on `stream`, no host sync.  EINVAL for bad sizes, NULL or
+ * misaligned pointers. */
 int wenc_cross_attend(wenc_t *h, const void *q, const void *xk, const void *xv, int32_t batch, int32_t n_q,
                       int32_t n_ctx, void *out, void *stream);
 
