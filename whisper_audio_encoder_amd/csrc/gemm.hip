@@ -23,10 +23,9 @@
 // two, with one barrier per step.  The 256 x 256 kernel runs a ping-pong
 // schedule: the two waves sharing a SIMD work a phase apart, one issuing a
 // step's MFMAs while the other reads its fragments from LDS and issues
-// transfers (details at the main loop).  The MFMA takes W as its A operand
-// and A^T as its B operand, so each lane ends up owning one output row and
-// runs of 4 consecutive output columns, which the epilogues store as 8- or
-// 16-byte vectors.
+// transfers (details at the main loop).  The MFMA takes W as its A operand and A^T as its B operand, so
+// each lane ends up owning one output row and runs of 4 consecutive output
+// columns, which the epilogues store as 8- or 16-byte vectors.
 //
 // Workgroup ids are remapped so that each XCD (ids are dealt round-robin
 // over the 8 XCDs) receives a contiguous run of tiles, ordered in groups of
